@@ -1,0 +1,232 @@
+/*
+ * zaya.h — C ABI of the ZAYA1 decoder-block forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the ZAYA1 decoder layer as the nnterp encyclopedia page for
+ * nnterp.families.zaya ("ZAYA1") describes it:
+ *   h   = merge_a(self_attn(input_layernorm(x)), x)            ("The Notes / The block, in order")
+ *   out = merge_m(mlp(post_attention_layernorm(h)), h)
+ *   merge(o, r) = (o + hidden_states_bias) * hidden_states_scale + (r + residual_bias) * residual_scale
+ * with compressed convolutional attention ("Queries and keys are convolved, normed to
+ * √head_dim and the keys scaled"), grouped-query attention, and a top-1 mixture of
+ * SwiGLU experts beside a skip class whose router state carries from block to block
+ * ("One expert per token, chosen beside a skip class"). The stream is float32; every
+ * other tensor is in the load dtype ("The stream is float32 whatever the load").
+ * The decode state per attention layer is the KV cache plus conv_state [B, C, 2] and
+ * prev_hs [B, H] (JANGTQ2 model card, "Architecture Summary").
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev or documented as device point to device memory of the
+ *    current HIP device; host pointers are documented as such.
+ *  - All memory is owned by the caller. The library allocates nothing, keeps no
+ *    global state and is re-entrant; each call enqueues work on `stream` (a
+ *    hipStream_t passed as void*; NULL = the null stream) and returns without
+ *    waiting for it.
+ *  - Every check happens on the host before the first launch: on any error nothing
+ *    is enqueued and no output is written. The return value is ZAYA_OK (0) or one of
+ *    the negative ZAYA_E* codes; zaya_last_error() gives the message of the calling
+ *    thread's last failure.
+ *  - Layouts are dense, row-major, innermost dimension last.
+ *  - act = the load dtype of the configuration (ZAYA_BF16 or ZAYA_F32).
+ */
+#ifndef ZAYA_H_
+#define ZAYA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZAYA_ABI_VERSION 1
+
+enum zaya_dtype { ZAYA_F32 = 0, ZAYA_BF16 = 1 };
+
+enum zaya_status {
+  ZAYA_OK = 0,
+  ZAYA_EINVAL = -1,     /* a required pointer is NULL, or B/S <= 0 */
+  ZAYA_ESHAPE = -2,     /* configuration outside what the kernels support */
+  ZAYA_EDTYPE = -3,     /* unknown act dtype */
+  ZAYA_EWORKSPACE = -4, /* workspace NULL or smaller than the *_workspace_bytes query */
+  ZAYA_ECACHE = -5,     /* cache_len[b] < 0 or cache_len[b] + S > cap */
+  ZAYA_EALIAS = -6,     /* an output aliases an input it must not alias */
+  ZAYA_EHIP = -7        /* a HIP launch failed */
+};
+
+/* Block shape ("Config" and "Printout" on the nnterp page). Supported: head_dim in
+ * {64, 128}; n_heads % n_kv_heads == 0 with n_heads / n_kv_heads in {1, 2, 4, 8};
+ * rope_dim even and <= head_dim; conv_k == 3; n_experts + 1 <= 64; hidden,
+ * expert_inter and router_hidden multiples of 64; router_hidden == 256. */
+typedef struct zaya_block_config {
+  int hidden;          /* H (hidden_size) */
+  int n_heads;         /* query heads (num_attention_heads) */
+  int n_kv_heads;      /* key/value heads (num_key_value_heads) */
+  int head_dim;        /* d */
+  int rope_dim;        /* rotated leading dims of each head (partial_rotary_factor * d) */
+  float rope_theta;    /* rotary base */
+  int conv_k;          /* causal conv kernel over the q/k channels; must be 3 */
+  int n_experts;       /* E routed experts; the router scores E + 1 classes (last = skip) */
+  int expert_inter;    /* I (moe_intermediate_size) */
+  int router_hidden;   /* R (router down_proj width) */
+  int sliding_window;  /* < 0: off; else key k visible from query q iff 0 <= p_q - p_k <= window */
+  float rms_eps;       /* rms_norm_eps */
+  int act_dtype;       /* enum zaya_dtype */
+} zaya_block_config;
+
+/* Device pointers to one block's parameters, act dtype unless noted.
+ * W_qkv [n_heads*d + n_kv_heads*d + 2*(n_kv_heads*d/2), H]: rows q_proj, k_proj,
+ *   v_proj_current, v_proj_delayed ("Printout": ZayaCCAProjection).
+ * conv_w [C, 3], conv_b [C], C = (n_heads + n_kv_heads) * d: the q channels (head-major)
+ *   then the k channels; tap 2 multiplies the current token.
+ * temp [n_kv_heads]: key temperature. W_o [H, n_heads*d].
+ * a_* / m_* [H]: hidden_states_bias (hsb), hidden_states_scale (hss), residual_bias
+ *   (rb), residual_scale (rs) of the attention and MoE merges.
+ * r_Wd [R, H], r_bd [R], r_rss [R] (router_states_scale), r_norm_g [R], r_W1, r_W2
+ *   [R, R], r_b1, r_b2 [R], r_Wout [E+1, R].
+ * bal_bias: fp32 [E+1] (balancing_biases). W_gu [E, 2I, H]: gate rows then up rows.
+ * W_dn [E, H, I]. */
+typedef struct zaya_block_weights {
+  const void* ln1_g;
+  const void* W_qkv;
+  const void* conv_w;
+  const void* conv_b;
+  const void* temp;
+  const void* W_o;
+  const void* a_hsb;
+  const void* a_hss;
+  const void* a_rb;
+  const void* a_rs;
+  const void* ln2_g;
+  const void* r_Wd;
+  const void* r_bd;
+  const void* r_rss;
+  const void* r_norm_g;
+  const void* r_W1;
+  const void* r_b1;
+  const void* r_W2;
+  const void* r_b2;
+  const void* r_Wout;
+  const float* bal_bias;
+  const void* W_gu;
+  const void* W_dn;
+  const void* m_hsb;
+  const void* m_hss;
+  const void* m_rb;
+  const void* m_rs;
+} zaya_block_weights;
+
+/* Per-block decode state (JANGTQ2 card, "Architecture Summary"): the KV cache plus
+ * conv_state and prev_hs. K, V [B, n_kv_heads, cap, d]; new tokens are written at
+ * positions cache_len[b] .. cache_len[b]+S-1. conv_state [B, C, 2]: slot 0 = the
+ * q/k conv input two tokens back, slot 1 = one token back. prev_hs [B, H]: the
+ * previous token's normed input (attention_norm_output). A sequence with
+ * cache_len[b] == 0 is fresh: its history reads as zeros whatever the buffers hold.
+ * conv_state and prev_hs are updated in place; cache_len is never written (the
+ * caller advances it). cache_len is a host array (required); cache_len_dev is an
+ * optional device copy of the same values (if NULL the library stages a copy in the
+ * workspace with an asynchronous host-to-device copy). */
+typedef struct zaya_cca_cache {
+  void* K;
+  void* V;
+  int cap;
+  void* conv_state;
+  void* prev_hs;
+  const int32_t* cache_len;
+  const int32_t* cache_len_dev;
+} zaya_cca_cache;
+
+/* Optional debug taps, named after "The API / support()" on the nnterp page. Each
+ * non-NULL pointer (device) receives a copy; NULL taps cost nothing.
+ * T = B*S rows; layouts:
+ *   attention_norm_output, mlp_norm_output [B,S,H] act; attention_queries [B,nh,S,d];
+ *   attention_keys, attention_values [B,nkv,S,d]; attention_premix [B,S,nh*d];
+ *   attention_output [B,S,H] act; layer_mid [B,S,H] fp32; router_logits [B,S,E+1] act;
+ *   expert_classes [B,S] int32 (E = skip); expert_indices [B,S] int32;
+ *   expert_weights [B,S] act; bucket_offsets [E+1] int32; bucket_ids [T] int32 (first
+ *   bucket_offsets[E] used); mlp_neurons [T, I] act in bucket order; routed_output,
+ *   mlp_output [B,S,H] act. */
+typedef struct zaya_taps {
+  void* attention_norm_output;
+  void* attention_queries;
+  void* attention_keys;
+  void* attention_values;
+  void* attention_premix;
+  void* attention_output;
+  float* layer_mid;
+  void* mlp_norm_output;
+  void* router_logits;
+  int32_t* expert_classes;
+  int32_t* expert_indices;
+  void* expert_weights;
+  int32_t* bucket_offsets;
+  int32_t* bucket_ids;
+  void* mlp_neurons;
+  void* routed_output;
+  void* mlp_output;
+} zaya_taps;
+
+/* Workspace (device bytes) needed by one block call of B sequences of S tokens
+ * (decode != 0: the zaya_block_decode path, S must be 1). Returns 0 for an invalid
+ * configuration. The workspace needs 256-byte alignment. */
+size_t zaya_block_workspace_bytes(const zaya_block_config* cfg, int B, int S, int decode);
+
+/* One block forward over B sequences of S new tokens.
+ * x [B,S,H] fp32 (device; must not alias x_out). router_state_in [B,S,R] act: the
+ * previous block's router state (NULL = block-0 semantics: no state is added).
+ * x_out [B,S,H] fp32: layer_output. router_state_out [B,S,R] act: the state handed
+ * to the next block (may not alias router_state_in). cache: the decode state; may be
+ * NULL for fresh sequences (then keys and values live in the workspace).
+ * taps: NULL or debug outputs. */
+int zaya_block_prefill(const zaya_block_config* cfg, const zaya_block_weights* w, int B, int S,
+                       const float* x, const void* router_state_in, float* x_out, void* router_state_out,
+                       const zaya_cca_cache* cache, const zaya_taps* taps, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* One decode step: one new token per sequence (S = 1). x [B,H] fp32;
+ * router_state_in/out [B,R]; cache required. Same contract as zaya_block_prefill. */
+int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w, int B, const float* x,
+                      const void* router_state_in, float* x_out, void* router_state_out,
+                      const zaya_cca_cache* cache, const zaya_taps* taps, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Stack: embedding (tied with lm_head), n_layers blocks, final norm, lm_head
+ * ("The block": embed_tokens -> layers x 40 -> norm -> lm_head; "The stream is float32
+ * whatever the load": the embedding is shifted and scaled, then cast to fp32;
+ * "The readout and the tokenizer": no cap or scale on the logits). */
+typedef struct zaya_stack_config {
+  zaya_block_config block;
+  int n_layers;
+  int vocab;
+} zaya_stack_config;
+
+/* embed [vocab, H] act (also the lm_head weight), emb_shift [H], emb_scale [H],
+ * final_g [H]; blocks: host array of n_layers weight structs (device pointers). */
+typedef struct zaya_stack_weights {
+  const void* embed;
+  const void* emb_shift;
+  const void* emb_scale;
+  const void* final_g;
+  const zaya_block_weights* blocks;
+} zaya_stack_weights;
+
+size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S);
+
+/* ids [B,S] int32 device, each in [0, vocab) (ids outside read row 0 — never out of
+ * bounds); logits [B,S,vocab] act device. caches: NULL, or a host array of n_layers
+ * cache structs. taps: NULL or a host array of n_layers tap structs. */
+int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w, int B, int S,
+                       const int32_t* ids, void* logits, const zaya_cca_cache* caches, const zaya_taps* taps,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* zaya_last_error(void);
+/* Name of a status code. */
+const char* zaya_status_str(int status);
+/* ZAYA_ABI_VERSION of the built library. */
+int zaya_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZAYA_H_ */

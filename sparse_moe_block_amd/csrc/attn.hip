@@ -1,0 +1,479 @@
+// Grouped-query attention over the CCA queries/keys/values.
+//
+// Semantics ("The API / support()": attention_scores masked, softmax, pattern times
+// values; "Config": 8 query heads over 2 KV heads; "Queries and keys are convolved
+// ..." for the window): query head h reads KV head h / (nh/nkv); score = q.k / sqrt(d);
+// key k is visible from query q iff p_k <= p_q and, with a window W >= 0,
+// p_q - p_k <= W. Softmax in fp32 (online, base 2), output rounded to act.
+//
+// Prefill kernel: one workgroup per (32-query tile, KV group, sequence) with one wave
+// per query head of the group, so the four heads share every K/V tile staged in LDS.
+// Both products run on MFMA: S^T = K Q^T (each lane then holds 16 scores of one
+// query row, so row statistics need only two cross-lane steps) and O^T = V^T P^T,
+// where P is fed straight from the score registers and V is transposed as it is
+// written into LDS. Tiles entirely outside the causal/window band are skipped; only
+// tiles that cut the band are masked element by element.
+//
+// Decode kernel (one new token per sequence): split over the cached keys — one
+// workgroup per (256-key chunk, KV group, sequence), one wave per query head, K/V
+// tiles staged through LDS with 16-byte coalesced loads, scores with one lane per key,
+// the weighted sum with one lane per pair of dims — then a combine pass merges the
+// chunks' (max, sum, partial output) triples.
+#include "common.h"
+#include "kernels.h"
+
+namespace zaya {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ----------------------------------------------------------------------------- prefill
+
+template <typename T, int D>
+struct AttnLds {
+  static constexpr int kKeys = 64;
+  static constexpr int kKRow = D * (int)sizeof(T) + 16;   // K tile row stride (bytes)
+  static constexpr int kVRow = kKeys * (int)sizeof(T) + 16;  // V^T tile row stride (bytes)
+  static constexpr int kKBytes = kKeys * kKRow;
+  static constexpr int kVBytes = D * kVRow;
+  static constexpr int kBytes = kKBytes + kVBytes;
+};
+
+// Global -> registers for one 64-key tile: K rows as 16-byte chunks, V as 4-key x 8-dim
+// blocks (so the transposed LDS write packs four keys per store).
+template <typename T, int D>
+struct TileRegs {
+  static constexpr int kElem16 = 16 / (int)sizeof(T);            // elements per 16 bytes
+  static constexpr int kKChunks = 64 * D / kElem16;              // 16-byte chunks in the K tile
+  static constexpr int kVTasks = 16 * (D / 8);                   // (key quad, 8-dim block) tasks
+};
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void attn_load_tile(const T* Kb, const T* Vb, int k0, int kvalid, uint4* kr, uint4* vr) {
+  using TR = TileRegs<T, D>;
+  constexpr int KC = (TR::kKChunks + NT - 1) / NT;
+  constexpr int VT = (TR::kVTasks + NT - 1) / NT;
+  constexpr int per_row = D / TR::kElem16;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int c = threadIdx.x + i * NT;
+    const int key = c / per_row, col = (c % per_row) * TR::kElem16;
+    kr[i] = (c < TR::kKChunks && k0 + key < kvalid)
+                ? *reinterpret_cast<const uint4*>(Kb + (size_t)(k0 + key) * D + col)
+                : make_uint4(0, 0, 0, 0);
+  }
+  // V: task = (quad q4, block db8): keys 4*q4..+3, dims 8*db8..+7 -> 4 rows x (8 elements)
+  constexpr int VW = 8 * (int)sizeof(T) / 16;  // 16-byte words per 8 elements (1 or 2)
+#pragma unroll
+  for (int i = 0; i < VT; ++i) {
+    const int task = threadIdx.x + i * NT;
+    const int q4 = task / (D / 8), db8 = task % (D / 8);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        const int key = 4 * q4 + kk;
+        vr[(i * 4 + kk) * VW + w] = (task < TR::kVTasks && k0 + key < kvalid)
+                                        ? *reinterpret_cast<const uint4*>(Vb + (size_t)(k0 + key) * D + db8 * 8 + w * TR::kElem16)
+                                        : make_uint4(0, 0, 0, 0);
+      }
+  }
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void attn_store_tile(char* lds, const uint4* kr, const uint4* vr) {
+  using TR = TileRegs<T, D>;
+  using L = AttnLds<T, D>;
+  constexpr int KC = (TR::kKChunks + NT - 1) / NT;
+  constexpr int VT = (TR::kVTasks + NT - 1) / NT;
+  constexpr int per_row = D / TR::kElem16;
+  constexpr int VW = 8 * (int)sizeof(T) / 16;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int c = threadIdx.x + i * NT;
+    if (c < TR::kKChunks) {
+      const int key = c / per_row, colb = (c % per_row) * 16;
+      *reinterpret_cast<uint4*>(lds + key * L::kKRow + colb) = kr[i];
+    }
+  }
+  char* vt = lds + L::kKBytes;
+#pragma unroll
+  for (int i = 0; i < VT; ++i) {
+    const int task = threadIdx.x + i * NT;
+    if (task >= TR::kVTasks) continue;
+    const int q4 = task / (D / 8), db8 = task % (D / 8);
+    // element j (0..7) of key kk lives in word (kk, j / kElem16), slot j % kElem16
+    const T* e[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) e[kk] = reinterpret_cast<const T*>(&vr[(i * 4 + kk) * VW]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      T* dst = reinterpret_cast<T*>(vt + (db8 * 8 + j) * L::kVRow) + 4 * q4;
+      if constexpr (sizeof(T) == 2) {
+        uint2 w;
+        w.x = (uint32_t)e[0][j] | ((uint32_t)e[1][j] << 16);
+        w.y = (uint32_t)e[2][j] | ((uint32_t)e[3][j] << 16);
+        *reinterpret_cast<uint2*>(dst) = w;
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(e[0][j], e[1][j], e[2][j], e[3][j]);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::frag load_vt_frag(const char* vt, int drow, int c, int grp) {
+  using L = AttnLds<T, D>;
+  const T* row = reinterpret_cast<const T*>(vt + drow * L::kVRow);
+  typename Mfma<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * c + 4 * grp);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * c + 16 + 4 * grp);
+    f.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  } else {
+    f.a = *reinterpret_cast<const float4*>(row + 32 * c + 4 * grp);
+    f.b = *reinterpret_cast<const float4*>(row + 32 * c + 16 + 4 * grp);
+  }
+  return f;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
+  using MF = Mfma<T>;
+  using frag = typename MF::frag;
+  using L = AttnLds<T, D>;
+  constexpr int NT = 64 * G;
+  constexpr int DC = D / 32;  // 32-wide K chunks of the QK product
+  constexpr int DB = D / 16;  // 16-row output blocks of O^T
+  __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
+
+  const int nqb = gridDim.x;
+  const int qblk = nqb - 1 - (int)blockIdx.x;  // heavy (late) query tiles first
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = g * G + wave;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int S = a.S, L0 = a.cache_len[b];
+  const int q0 = qblk * 32;
+  const int nq = min(32, S - q0);
+  const int qp_min = L0 + q0, qp_max = L0 + q0 + nq - 1;
+  const int W = a.window;
+
+  // queries of this head: rows q0 + qb*16 + r16
+  frag qf[2][DC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int t = q0 + qb * 16 + r16;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qf[qb][dc] = t < S ? MF::load(a.Q + (((size_t)b * S + t) * a.nh + h) * D + dc * 32 + grp * 8) : MF::zero();
+  }
+
+  f32x4 o[2][DB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  const int klo = W >= 0 ? max(0, qp_min - W) : 0;
+  const int kt_begin = klo / 64, kt_end = qp_max / 64 + 1;
+  const int kvalid = L0 + S;
+  const T* Kb = a.K + ((size_t)b * a.nkv + g) * a.cap * D;
+  const T* Vb = a.V + ((size_t)b * a.nkv + g) * a.cap * D;
+  const float sscale = kLog2e / sqrtf((float)D);
+
+  using TR = TileRegs<T, D>;
+  constexpr int KC = (TR::kKChunks + NT - 1) / NT;
+  constexpr int VT = (TR::kVTasks + NT - 1) / NT;
+  constexpr int VW = 8 * (int)sizeof(T) / 16;
+  uint4 kr[KC], vr[VT * 4 * VW];
+  attn_load_tile<T, D, NT>(Kb, Vb, kt_begin * 64, kvalid, kr, vr);
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    __syncthreads();  // previous tile fully consumed
+    attn_store_tile<T, D, NT>(lds, kr, vr);
+    __syncthreads();
+    if (kt + 1 < kt_end) attn_load_tile<T, D, NT>(Kb, Vb, (kt + 1) * 64, kvalid, kr, vr);
+    const int k0 = kt * 64;
+
+    // S^T = K Q^T: s[qb][kb] holds S[q = qb*16 + r16][key = k0 + kb*16 + 4*grp + i]
+    f32x4 s[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const frag kf = MF::load(reinterpret_cast<const T*>(lds + (kb * 16 + r16) * L::kKRow) + dc * 32 + grp * 8);
+        s[0][kb] = MF::mma(kf, qf[0][dc], s[0][kb]);
+        s[1][kb] = MF::mma(kf, qf[1][dc], s[1][kb]);
+      }
+
+    const bool full = (k0 + 63 <= qp_min) && (W < 0 || qp_max - k0 <= W);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qp = L0 + q0 + qb * 16 + r16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[qb][kb][i] * sscale;
+          if (!full) {
+            const int kp = k0 + kb * 16 + 4 * grp + i;
+            if (kp > qp || (W >= 0 && qp - kp > W)) v = -INFINITY;
+          }
+          s[qb][kb][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run[qb] - m_use);
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = exp2f(s[qb][kb][i] - m_use);
+          s[qb][kb][i] = pv;
+          ps += pv;
+        }
+      l_run[qb] = l_run[qb] * alpha + ps;
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
+    }
+
+    // O^T += V^T P^T over two 32-key chunks
+    const char* vt = lds + L::kKBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      frag pf[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float pv[8] = {s[qb][2 * c][0],     s[qb][2 * c][1],     s[qb][2 * c][2],     s[qb][2 * c][3],
+                             s[qb][2 * c + 1][0], s[qb][2 * c + 1][1], s[qb][2 * c + 1][2], s[qb][2 * c + 1][3]};
+        pf[qb] = MF::pack(pv);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const frag vf = load_vt_frag<T, D>(vt, db * 16 + r16, c, grp);
+        o[0][db] = MF::mma(vf, pf[0], o[0][db]);
+        o[1][db] = MF::mma(vf, pf[1], o[1][db]);
+      }
+    }
+  }
+
+  // finalize: O[q][d] /= row sum; lane holds d = db*16 + 4*grp + i of query r16
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = l_run[qb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int t = q0 + qb * 16 + r16;
+    if (t < S) {
+      T* orow = a.O + (((size_t)b * S + t) * a.nh + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        float v[4] = {o[qb][db][0] * inv, o[qb][db][1] * inv, o[qb][db][2] * inv, o[qb][db][3] * inv};
+        store4(orow + db * 16 + 4 * grp, v);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- decode
+
+constexpr int kDecChunkMin = 256;   // keys per decode chunk, at least
+constexpr int kDecChunksMax = 128;  // chunks per (sequence, KV group), at most
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, float* __restrict__ part, int nchunk,
+                                                             int chunk) {
+  constexpr int NT = 64 * G;
+  constexpr int KROW = D * (int)sizeof(T) + 16;
+  constexpr int VROW = D * (int)sizeof(T);
+  constexpr int DPL = D / 64;  // dims per lane in the weighted sum
+  __shared__ __attribute__((aligned(16))) char kt_s[64 * KROW];
+  __shared__ __attribute__((aligned(16))) char vt_s[64 * VROW];
+  __shared__ float q_s[G][D];
+  __shared__ float p_s[G][64];
+
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = g * G + wave;
+  const int L0 = a.cache_len[b];
+  const int qp = L0;  // the new token's position
+  const int kvalid = L0 + 1;
+  const int W = a.window;
+  const int klo = W >= 0 ? max(0, qp - W) : 0;
+  const int c_lo = max(klo, c * chunk), c_hi = min(kvalid, (c + 1) * chunk);
+  const float sscale = kLog2e / sqrtf((float)D);
+
+  for (int i = lane; i < D; i += 64) q_s[wave][i] = Act<T>::tof(a.Q[((size_t)b * a.nh + h) * D + i]);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.f;
+
+  const T* Kb = a.K + ((size_t)b * a.nkv + g) * a.cap * D;
+  const T* Vb = a.V + ((size_t)b * a.nkv + g) * a.cap * D;
+  constexpr int E16 = 16 / (int)sizeof(T);
+  constexpr int CPR = D / E16;               // 16-byte chunks per row
+  constexpr int NCH = 64 * CPR;              // per tile, per tensor
+  constexpr int PER = (NCH + NT - 1) / NT;
+  for (int t0 = (c_lo / 64) * 64; t0 < c_hi; t0 += 64) {
+    uint4 kr[PER], vr[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      const int key = ch / CPR, col = (ch % CPR) * E16;
+      const bool ok = ch < NCH && t0 + key < c_hi;
+      kr[i] = ok ? *reinterpret_cast<const uint4*>(Kb + (size_t)(t0 + key) * D + col) : make_uint4(0, 0, 0, 0);
+      vr[i] = ok ? *reinterpret_cast<const uint4*>(Vb + (size_t)(t0 + key) * D + col) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // previous tile consumed (and q_s written on the first pass)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      if (ch < NCH) {
+        const int key = ch / CPR, colb = (ch % CPR) * 16;
+        *reinterpret_cast<uint4*>(kt_s + key * KROW + colb) = kr[i];
+        *reinterpret_cast<uint4*>(vt_s + key * VROW + colb) = vr[i];
+      }
+    }
+    __syncthreads();
+    // scores: lane = key
+    const int kp = t0 + lane;
+    const T* krow = reinterpret_cast<const T*>(kt_s + lane * KROW);
+    float acc = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D; i += 4) {
+      float kv[4];
+      load4(krow + i, kv);
+      acc += q_s[wave][i] * kv[0] + q_s[wave][i + 1] * kv[1] + q_s[wave][i + 2] * kv[2] + q_s[wave][i + 3] * kv[3];
+    }
+    const bool vis = kp >= c_lo && kp < c_hi;
+    const float sv = vis ? acc * sscale : -INFINITY;
+    const float mx = wave_max(sv);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    const float pv = exp2f(sv - m_use);
+    l_run = l_run * alpha + pv;
+    m_run = m_new;
+    p_s[wave][lane] = pv;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[j] *= alpha;
+    for (int k = 0; k < 64; ++k) {
+      const float pk = p_s[wave][k];
+      const T* vrow = reinterpret_cast<const T*>(vt_s + k * VROW);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[j] += pk * Act<T>::tof(vrow[lane * DPL + j]);
+    }
+  }
+  l_run = wave_sum(l_run);
+  float* pp = part + ((((size_t)b * a.nkv + g) * nchunk + c) * G + wave) * (D + 2);
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) pp[lane * DPL + j] = o[j];
+  if (lane == 0) {
+    pp[D] = m_run;
+    pp[D + 1] = l_run;
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnArgs<T> a, const float* __restrict__ part,
+                                                                  int nchunk) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.nh, h = bh % a.nh;
+  const int g = h / G, w = h % G;
+  const float* base = part + (((size_t)b * a.nkv + g) * nchunk * G + w) * (D + 2);
+  const size_t stride = (size_t)G * (D + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, base[c * stride + D]);
+  float lsum = 0.f;
+  float acc[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const float* pc = base + c * stride;
+    const float mc = pc[D];
+    const float sc = mc == -INFINITY ? 0.f : exp2f(mc - M);
+    lsum += sc * pc[D + 1];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) acc[j] += sc * pc[threadIdx.x * (D / 64) + j];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  T* orow = a.O + ((size_t)b * a.nh + h) * D;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) orow[threadIdx.x * (D / 64) + j] = Act<T>::cvt(acc[j] * inv);
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_prefill_dg(const AttnArgs<T>& a, hipStream_t s) {
+  dim3 grid((a.S + 31) / 32, a.nkv, a.B);
+  hipLaunchKernelGGL((attn_prefill_kernel<T, D, G>), grid, dim3(64 * G), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_decode_dg(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s) {
+  int nchunk = min(kDecChunksMax, (maxlen + kDecChunkMin - 1) / kDecChunkMin);
+  const int chunk = (((maxlen + nchunk - 1) / nchunk) + 63) / 64 * 64;
+  nchunk = (maxlen + chunk - 1) / chunk;
+  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), dim3(nchunk, a.nkv, a.B), dim3(64 * G), 0, s, a, part, nchunk,
+                     chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_decode_combine_kernel<T, D, G>), dim3(a.B * a.nh), dim3(64), 0, s, a, part, nchunk);
+  return hipGetLastError();
+}
+
+#define ZAYA_DISPATCH_DG(FN, ...)                                 \
+  do {                                                            \
+    const int G_ = a.nh / a.nkv;                                  \
+    if (a.d == 128) {                                             \
+      if (G_ == 1) return FN<T, 128, 1>(__VA_ARGS__);             \
+      if (G_ == 2) return FN<T, 128, 2>(__VA_ARGS__);             \
+      if (G_ == 4) return FN<T, 128, 4>(__VA_ARGS__);             \
+      if (G_ == 8) return FN<T, 128, 8>(__VA_ARGS__);             \
+    } else if (a.d == 64) {                                       \
+      if (G_ == 1) return FN<T, 64, 1>(__VA_ARGS__);              \
+      if (G_ == 2) return FN<T, 64, 2>(__VA_ARGS__);              \
+      if (G_ == 4) return FN<T, 64, 4>(__VA_ARGS__);              \
+      if (G_ == 8) return FN<T, 64, 8>(__VA_ARGS__);              \
+    }                                                             \
+    return hipErrorInvalidValue;                                  \
+  } while (0)
+
+template <typename T>
+hipError_t launch_attn_prefill(const AttnArgs<T>& a, hipStream_t s) {
+  ZAYA_DISPATCH_DG(launch_prefill_dg, a, s);
+}
+
+template <typename T>
+hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s) {
+  ZAYA_DISPATCH_DG(launch_decode_dg, a, part, maxlen, s);
+}
+
+size_t attn_decode_part_bytes(int B, int nkv, int G, int d) {
+  return (size_t)B * nkv * kDecChunksMax * G * (d + 2) * sizeof(float);
+}
+
+template hipError_t launch_attn_prefill<bf16_t>(const AttnArgs<bf16_t>&, hipStream_t);
+template hipError_t launch_attn_prefill<float>(const AttnArgs<float>&, hipStream_t);
+template hipError_t launch_attn_decode<bf16_t>(const AttnArgs<bf16_t>&, float*, int, hipStream_t);
+template hipError_t launch_attn_decode<float>(const AttnArgs<float>&, float*, int, hipStream_t);
+
+}  // namespace zaya

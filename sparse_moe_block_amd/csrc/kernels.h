@@ -1,0 +1,129 @@
+// Internal launch interface between the C ABI (zaya_api.cpp) and the kernels.
+// Every launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace zaya {
+
+// ---- norms / embedding
+template <typename T>
+hipError_t launch_rmsnorm_stream(const float* x, const T* g, T* out, int rows, int H, float eps, hipStream_t s);
+template <typename T>
+hipError_t launch_embed(const int32_t* ids, const T* table, const T* shift, const T* scale, float* x0, T* tap,
+                        int rows, int H, int vocab, hipStream_t s);
+
+// ---- dense GEMMs (A [M,K] rows, B [N,K] rows)
+template <typename T>
+hipError_t launch_gemm_store(const T* A, int lda, const T* B, int ldb, int M, int N, int K, T* C, int ldc,
+                             hipStream_t s);
+template <typename T>
+hipError_t launch_gemm_merge(const T* O, const T* Wo, int M, int H, int K, const float* x, const T* hsb, const T* hss,
+                             const T* rb, const T* rs, float* h, T* a_tap, hipStream_t s);
+template <typename T>
+hipError_t launch_gemm_router_in(const T* hn, const T* Wd, int M, int R, int H, const T* b, const T* rss,
+                                 const T* s_in, T* u, hipStream_t s);
+
+// ---- CCA projection
+template <typename T>
+struct CcaArgs {
+  const T* P;  // [T, qkv_ld] projections of every new token
+  int qkv_ld;
+  const T* vdp;  // [B, nkv*d/2] prev_hs @ W_vd^T
+  const T* conv_w;
+  const T* conv_b;
+  const T* temp;
+  T* conv_state;  // [B, C, 2] in/out
+  T* prev_hs;     // [B, H] out
+  const T* xn;    // [T, H] normed input (source of the new prev_hs)
+  const int32_t* cache_len;  // device [B]
+  T* Q;  // [T, nh, d]
+  T* K;  // [B, nkv, cap, d]
+  T* V;
+  int cap;
+  T* q_tap;  // [B, nh, S, d] or NULL
+  T* k_tap;  // [B, nkv, S, d] or NULL
+  T* v_tap;
+  int B, S, H, nh, nkv, d, rope_dim, C;
+  float theta;
+};
+template <typename T>
+hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s);
+
+// ---- attention
+template <typename T>
+struct AttnArgs {
+  const T* Q;  // [B, S, nh, d]
+  const T* K;  // [B, nkv, cap, d]
+  const T* V;
+  T* O;  // [B, S, nh, d]
+  const int32_t* cache_len;  // device [B]
+  int B, S, nh, nkv, d, cap, window;
+};
+template <typename T>
+hipError_t launch_attn_prefill(const AttnArgs<T>& a, hipStream_t s);
+template <typename T>
+hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s);
+size_t attn_decode_part_bytes(int B, int nkv, int G, int d);
+
+// ---- router MLP + selection (+ skip-token merge)
+template <typename T>
+struct RouterArgs {
+  const T* u;  // [T, R] router state after the carried-state add
+  const T* norm_g;
+  const T* W1;
+  const T* b1;
+  const T* W2;
+  const T* b2;
+  const T* Wout;  // [E+1, R]
+  const float* bal_bias;
+  T* logits;  // [T, E+1]
+  int32_t* cls;
+  int32_t* idx;
+  T* wts;
+  const float* h;  // [T, H] stream after the attention merge
+  const T* m_hsb;
+  const T* m_hss;
+  const T* m_rb;
+  const T* m_rs;
+  float* out;      // [T, H] layer output (skip tokens written here)
+  T* routed_tap;   // [T, H] or NULL
+  T* mlp_tap;      // [T, H] or NULL
+  int ntok, R, E, H;
+  float eps;
+};
+template <typename T>
+hipError_t launch_router(const RouterArgs<T>& a, hipStream_t s);
+
+// ---- mixture of experts
+hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, int32_t* ids, hipStream_t s);
+
+template <typename T>
+struct MoeArgs {
+  const int32_t* offsets;  // [E+1]
+  const int32_t* ids;      // [ntok] (first offsets[E] used)
+  const T* hn;             // [ntok, H]
+  const T* W_gu;           // [E, 2I, H]
+  const T* W_dn;           // [E, H, I]
+  T* neurons;              // [ntok, I] bucket order
+  const T* wts;            // [ntok]
+  const float* h;          // [ntok, H]
+  const T* hsb;
+  const T* hss;
+  const T* rb;
+  const T* rs;
+  float* out;     // [ntok, H]
+  T* routed_tap;  // or NULL
+  T* mlp_tap;     // or NULL
+  int ntok, H, I, E;
+};
+template <typename T>
+hipError_t launch_moe(const MoeArgs<T>& a, hipStream_t s);
+
+// ---- small helpers
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);
+
+}  // namespace zaya

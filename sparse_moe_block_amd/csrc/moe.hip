@@ -1,0 +1,208 @@
+// Mixture of experts: token buckets, SwiGLU experts, weighted combine and merge.
+//
+// ("One expert per token, chosen beside a skip class", "Ablating an expert leaves the
+// merge's bias" and "The API / support()" — mlp_activation, mlp_neurons,
+// expert_outputs, routed_output, mlp_output — on the nnterp page; "Printout":
+// ZayaExperts with SiLU; the experts are pre-stacked per the JANGTQ2 card.)
+//
+//   bucket:  ids = routed tokens grouped by expert, ascending within an expert
+//            (stable), offsets = exclusive prefix of the per-expert counts; skip
+//            tokens belong to no bucket.
+//   gate/up: act = rnd(silu(rnd(x Wg^T))), neurons = rnd(act * rnd(x Wu^T))
+//   down:    y = rnd(neurons Wd^T); routed = rnd(w * y)
+//            mlp_output = rnd(rnd(routed + hsb) * hss); out = f32(f32(h + rb) * rs) + mlp_output
+//
+// Grouped GEMMs: the grid is (n tiles) x (an upper bound on the number of row tiles
+// over all experts, ceil(T/BM) + E); each workgroup walks the E+1 offsets to find
+// its (expert, row tile) and exits if it has none, so nothing waits on the host.
+// Gate and up weight rows are interleaved in 16-row blocks inside each weight tile,
+// so every lane holds a gate and an up accumulator for the same outputs and SwiGLU
+// happens in registers.
+#include "common.h"
+#include "gemm_core.h"
+#include "kernels.h"
+
+namespace zaya {
+
+// ----------------------------------------------------------------------------- buckets
+
+__global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict__ cls, int ntok, int E,
+                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ ids) {
+  __shared__ int cnt[64];
+  __shared__ int base[64];
+  __shared__ int wcnt[16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 64) cnt[tid] = 0;
+  __syncthreads();
+  for (int t = tid; t < ntok; t += blockDim.x) {
+    const int c = cls[t];
+    if (c >= 0 && c < E) atomicAdd(&cnt[c], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      base[e] = run;
+      offsets[e] = run;
+      run += cnt[e];
+    }
+    offsets[E] = run;
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int chunk = 0; chunk < ntok; chunk += blockDim.x) {
+    const int t = chunk + tid;
+    const int c = t < ntok ? cls[t] : -1;
+    int rank = 0;
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot(c == e);
+      if (lane == 0) wcnt[wave][e] = __popcll(m);
+      if (c == e) rank = __popcll(m & lt);
+    }
+    __syncthreads();
+    if (c >= 0 && c < E) {
+      int pos = base[c] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][c];
+      ids[pos] = t;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) add += wcnt[w][tid];
+      base[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, int32_t* ids, hipStream_t s) {
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, cls, ntok, E, offsets, ids);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- grouped GEMMs
+
+// Map a row-tile slot to (expert, first row of the tile within the expert's bucket).
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off, int E, int BM, int slot, int& e_out,
+                                          int& r0_out, int& n_out) {
+  int cum = 0;
+  for (int e = 0; e < E; ++e) {
+    const int n = off[e + 1] - off[e];
+    const int nt = (n + BM - 1) / BM;
+    if (slot < cum + nt) {
+      e_out = e;
+      r0_out = (slot - cum) * BM;
+      n_out = n;
+      return true;
+    }
+    cum += nt;
+  }
+  return false;
+}
+
+template <typename T, int BM, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void moe_gateup_kernel(MoeArgs<T> a) {
+  constexpr int BN = 128;  // 64 activation columns: gate and up in alternating 16-row blocks
+  using Tile = GemmTile<T, BM, BN, WM, WN>;
+  static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
+  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  int e, r0, n_e;
+  if (!find_tile(a.offsets, a.E, BM, blockIdx.y, e, r0, n_e)) return;
+  const int j = blockIdx.x;  // activation columns [64j, 64j + 64)
+  const int base = a.offsets[e] + r0;
+  const int rows = min(BM, n_e - r0);
+  Tile t;
+  t.set_a([&](int r) -> const T* { return r < rows ? a.hn + (size_t)a.ids[base + r] * a.H : nullptr; });
+  const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
+  t.set_b([&](int r) -> const T* {
+    const int blk = r >> 4, w16 = r & 15;
+    const int row = ((blk & 1) ? a.I : 0) + 64 * j + (blk >> 1) * 16 + w16;
+    return Wg + (size_t)row * a.H;
+  });
+  t.run(smem, a.H / Tile::kBK);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+  for (int i = 0; i < Tile::kTM; ++i) {
+    const int m = wm * Tile::kTM * 16 + i * 16 + (lane & 15);
+    if (m >= rows) continue;
+    T* nrow = a.neurons + (size_t)(base + m) * a.I;
+#pragma unroll
+    for (int pp = 0; pp < Tile::kTN / 2; ++pp) {
+      const int col = 64 * j + (wn * (Tile::kTN / 2) + pp) * 16 + (lane >> 4) * 4;
+      float v[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float gt = Act<T>::rnd(t.acc[i][2 * pp][c]);
+        const float ut = Act<T>::rnd(t.acc[i][2 * pp + 1][c]);
+        const float act = Act<T>::rnd(gt / (1.0f + expf(-gt)));
+        v[c] = Act<T>::rnd(act * ut);
+      }
+      store4(nrow + col, v);
+    }
+  }
+}
+
+template <typename T, int BM, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void moe_down_kernel(MoeArgs<T> a) {
+  constexpr int BN = 128;
+  using Tile = GemmTile<T, BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  int e, r0, n_e;
+  if (!find_tile(a.offsets, a.E, BM, blockIdx.y, e, r0, n_e)) return;
+  const int n0 = blockIdx.x * BN;
+  const int base = a.offsets[e] + r0;
+  const int rows = min(BM, n_e - r0);
+  Tile t;
+  t.set_a([&](int r) -> const T* { return r < rows ? a.neurons + (size_t)(base + r) * a.I : nullptr; });
+  const T* Wd = a.W_dn + (size_t)e * a.H * a.I;
+  t.set_b([&](int r) -> const T* { return Wd + (size_t)(n0 + r) * a.I; });
+  t.run(smem, a.I / Tile::kBK);
+  t.epilogue([&](int m, int nl, const float* v) {
+    if (m >= rows) return;
+    const int tok = a.ids[base + m];
+    const int n = n0 + nl;
+    const float w = Act<T>::tof(a.wts[tok]);
+    float hv[4], b1[4], s1[4], b2[4], s2[4], ro[4], mo[4], o[4];
+    load4(a.h + (size_t)tok * a.H + n, hv);
+    load4(a.hsb + n, b1);
+    load4(a.hss + n, s1);
+    load4(a.rb + n, b2);
+    load4(a.rs + n, s2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float y = Act<T>::rnd(v[c]);
+      ro[c] = Act<T>::rnd(w * y);
+      mo[c] = Act<T>::rnd(Act<T>::rnd(ro[c] + b1[c]) * s1[c]);
+      o[c] = fadd(fmul(fadd(hv[c], b2[c]), s2[c]), mo[c]);
+    }
+    store4(a.out + (size_t)tok * a.H + n, o);
+    if (a.routed_tap) store4(a.routed_tap + (size_t)tok * a.H + n, ro);
+    if (a.mlp_tap) store4(a.mlp_tap + (size_t)tok * a.H + n, mo);
+  });
+}
+
+template <typename T, int BM, int WM, int WN>
+static hipError_t launch_moe_cfg(const MoeArgs<T>& a, hipStream_t s) {
+  const int slots = (a.ntok + BM - 1) / BM + a.E;
+  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN>), dim3(a.I / 64, slots), dim3(WM * WN * 64), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN>), dim3(a.H / 128, slots), dim3(WM * WN * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Row tile by load: 16-row tiles when experts see only a few tokens each (decode),
+// 128-row tiles otherwise.
+template <typename T>
+hipError_t launch_moe(const MoeArgs<T>& a, hipStream_t s) {
+  if (a.ntok <= 0) return hipSuccess;
+  if (a.ntok <= 32 * a.E) return launch_moe_cfg<T, 16, 1, 4>(a, s);
+  return launch_moe_cfg<T, 128, 2, 2>(a, s);
+}
+
+template hipError_t launch_moe<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);
+template hipError_t launch_moe<float>(const MoeArgs<float>&, hipStream_t);
+
+}  // namespace zaya

@@ -1,0 +1,109 @@
+// Stream RMSNorm and the embedding gather (HBM-bound; one wave per row).
+//
+// ZayaRMSNorm on the float32 stream ("The stream is float32 whatever the load" on the
+// nnterp page: the norm casts the stream to the weight dtype first, then norms it):
+//   xa = rnd(x);  y = rnd(xa / sqrt(mean(xa^2) + eps));  out = rnd(g * y)
+// Embedding ("The stream is float32 whatever the load": shift and scale, then the
+// cast to float32):  x0 = f32(rnd(rnd(E[id] + shift) * scale)).
+#include "common.h"
+#include "kernels.h"
+
+namespace zaya {
+
+// rows: number of rows; H % 256 == 0. Each lane owns H/256 groups of 4 consecutive
+// columns, strided 256 apart, so every wave-wide load is contiguous.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_stream_kernel(const float* __restrict__ x, const T* __restrict__ g,
+                                                               T* __restrict__ out, int rows, int H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* xr = x + (size_t)row * H;
+  T* orow = out + (size_t)row * H;
+  constexpr int kMaxGroups = 16;  // H <= 4096
+  float v[kMaxGroups][4];
+  const int ng = H / 256;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxGroups; ++i) {
+    if (i < ng) {
+      load4(xr + i * 256 + lane * 4, v[i]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[i][c] = Act<T>::rnd(v[i][c]);
+        ss += v[i][c] * v[i][c];
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < kMaxGroups; ++i) {
+    if (i < ng) {
+      float gv[4], o[4];
+      load4(g + i * 256 + lane * 4, gv);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(gv[c] * Act<T>::rnd(v[i][c] * inv));
+      store4(orow + i * 256 + lane * 4, o);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ table,
+                                                      const T* __restrict__ shift, const T* __restrict__ scale,
+                                                      float* __restrict__ x0, T* __restrict__ tap, int rows, int H,
+                                                      int vocab) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  int id = ids[row];
+  if (id < 0 || id >= vocab) id = 0;
+  const T* er = table + (size_t)id * H;
+  for (int c0 = lane * 4; c0 < H; c0 += 256) {
+    float e[4], sh[4], sc[4], o[4];
+    load4(er + c0, e);
+    load4(shift + c0, sh);
+    load4(scale + c0, sc);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(Act<T>::rnd(e[c] + sh[c]) * sc[c]);
+    store4(x0 + (size_t)row * H + c0, o);
+    if (tap) store4(tap + (size_t)row * H + c0, o);
+  }
+}
+
+template <typename T>
+hipError_t launch_rmsnorm_stream(const float* x, const T* g, T* out, int rows, int H, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_stream_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, x, g, out, rows, H, eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_embed(const int32_t* ids, const T* table, const T* shift, const T* scale, float* x0, T* tap,
+                        int rows, int H, int vocab, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, ids, table, shift, scale, x0, tap, rows,
+                     H, vocab);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rmsnorm_stream<bf16_t>(const float*, const bf16_t*, bf16_t*, int, int, float, hipStream_t);
+template hipError_t launch_rmsnorm_stream<float>(const float*, const float*, float*, int, int, float, hipStream_t);
+template hipError_t launch_embed<bf16_t>(const int32_t*, const bf16_t*, const bf16_t*, const bf16_t*, float*, bf16_t*,
+                                         int, int, int, hipStream_t);
+template hipError_t launch_embed<float>(const int32_t*, const float*, const float*, const float*, float*, float*, int,
+                                        int, int, hipStream_t);
+
+}  // namespace zaya

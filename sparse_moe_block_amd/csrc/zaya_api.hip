@@ -1,0 +1,405 @@
+// Host side of the C ABI declared in include/zaya.h: validation, workspace layout and
+// launch sequencing. No device call is made before every check has passed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/zaya.h"
+#include "kernels.h"
+
+using namespace zaya;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t act_bytes(const zaya_block_config* c) { return c->act_dtype == ZAYA_BF16 ? 2 : 4; }
+
+int check_config(const zaya_block_config* c) {
+  if (!c) return fail(ZAYA_EINVAL, "config is NULL");
+  if (c->act_dtype != ZAYA_BF16 && c->act_dtype != ZAYA_F32) return fail(ZAYA_EDTYPE, "act_dtype %d", c->act_dtype);
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->n_experts <= 0 ||
+      c->expert_inter <= 0 || c->router_hidden <= 0)
+    return fail(ZAYA_ESHAPE, "non-positive dimension");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(ZAYA_ESHAPE, "head_dim %d not in {64, 128}", c->head_dim);
+  if (c->n_heads % c->n_kv_heads) return fail(ZAYA_ESHAPE, "n_heads %% n_kv_heads != 0");
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ZAYA_ESHAPE, "n_heads / n_kv_heads = %d not in {1,2,4,8}", G);
+  if (c->rope_dim < 0 || c->rope_dim > c->head_dim || (c->rope_dim & 1))
+    return fail(ZAYA_ESHAPE, "rope_dim %d must be even and <= head_dim", c->rope_dim);
+  if (c->conv_k != 3) return fail(ZAYA_ESHAPE, "conv_k %d != 3", c->conv_k);
+  if (c->n_experts + 1 > 64) return fail(ZAYA_ESHAPE, "n_experts + 1 > 64");
+  if (c->hidden % 256 || c->hidden > 4096) return fail(ZAYA_ESHAPE, "hidden %d must be a multiple of 256, <= 4096", c->hidden);
+  if (c->expert_inter % 64) return fail(ZAYA_ESHAPE, "expert_inter %d must be a multiple of 64", c->expert_inter);
+  if (c->router_hidden != 256) return fail(ZAYA_ESHAPE, "router_hidden %d != 256", c->router_hidden);
+  if (!(c->rms_eps > 0.f)) return fail(ZAYA_ESHAPE, "rms_eps must be > 0");
+  if (!(c->rope_theta > 0.f)) return fail(ZAYA_ESHAPE, "rope_theta must be > 0");
+  return ZAYA_OK;
+}
+
+// Workspace layout of one block call.
+struct Plan {
+  size_t cache_len, xn, P, vdp, Q, Kw, Vw, convw, prevw, O, h, hn, logits, cls, idx, wts, offsets, ids, neurons, part;
+  size_t total;
+};
+
+Plan plan_block(const zaya_block_config* c, int B, int S, int decode) {
+  const size_t A = act_bytes(c);
+  const size_t T = (size_t)B * S;
+  const int H = c->hidden, nh = c->n_heads, nkv = c->n_kv_heads, d = c->head_dim;
+  const size_t QR = (size_t)nh * d + 2 * (size_t)nkv * d;
+  const int E = c->n_experts;
+  const size_t C = (size_t)(nh + nkv) * d;
+  Plan p{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  p.cache_len = take((size_t)B * 4);
+  p.xn = take(T * H * A);
+  p.P = take(T * QR * A);
+  p.vdp = take((size_t)B * nkv * (d / 2) * A);
+  p.Q = take(T * nh * d * A);
+  p.Kw = take(T * nkv * d * A);  // keys/values when the caller passes no cache
+  p.Vw = take(T * nkv * d * A);
+  p.convw = take((size_t)B * C * 2 * A);
+  p.prevw = take((size_t)B * H * A);
+  p.O = take(T * nh * d * A);
+  p.h = take(T * H * 4);
+  p.hn = take(T * H * A);
+  p.logits = take(T * (E + 1) * A);
+  p.cls = take(T * 4);
+  p.idx = take(T * 4);
+  p.wts = take(T * A);
+  p.offsets = take((size_t)(E + 1) * 4);
+  p.ids = take(T * 4);
+  p.neurons = take(T * c->expert_inter * A);
+  p.part = decode ? take(attn_decode_part_bytes(B, nkv, nh / nkv, d)) : take(0);
+  p.total = o;
+  return p;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int check_weights(const zaya_block_weights* w) {
+  if (!w) return fail(ZAYA_EINVAL, "weights is NULL");
+  const void* ptrs[] = {w->ln1_g, w->W_qkv, w->conv_w, w->conv_b, w->temp, w->W_o, w->a_hsb, w->a_hss, w->a_rb,
+                        w->a_rs, w->ln2_g, w->r_Wd, w->r_bd, w->r_rss, w->r_norm_g, w->r_W1, w->r_b1, w->r_W2,
+                        w->r_b2, w->r_Wout, w->bal_bias, w->W_gu, w->W_dn, w->m_hsb, w->m_hss, w->m_rb, w->m_rs};
+  for (size_t i = 0; i < sizeof ptrs / sizeof ptrs[0]; ++i)
+    if (!ptrs[i]) return fail(ZAYA_EINVAL, "weight pointer #%zu is NULL", i);
+  return ZAYA_OK;
+}
+
+#define HIPCHK(expr)                                                               \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess) return fail(ZAYA_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+template <typename T>
+int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, int S, bool decode, const float* x,
+              const void* s_in, float* x_out, void* s_out, const zaya_cca_cache* cache, const zaya_taps* taps,
+              char* ws, const Plan& p, int max_len, hipStream_t st) {
+  const int H = c->hidden, nh = c->n_heads, nkv = c->n_kv_heads, d = c->head_dim, E = c->n_experts;
+  const int I = c->expert_inter, R = c->router_hidden;
+  const int T_ = B * S;
+  const int QR = nh * d + 2 * nkv * d;
+  const int C = (nh + nkv) * d;
+  const size_t A = sizeof(T);
+  auto W = [](const void* q) { return static_cast<const T*>(q); };
+  T* xn = (T*)(ws + p.xn);
+  T* P = (T*)(ws + p.P);
+  T* vdp = (T*)(ws + p.vdp);
+  T* Q = (T*)(ws + p.Q);
+  T* O = (T*)(ws + p.O);
+  float* h = (float*)(ws + p.h);
+  T* hn = (T*)(ws + p.hn);
+  T* logits = (T*)(ws + p.logits);
+  int32_t* cls = (int32_t*)(ws + p.cls);
+  int32_t* idx = (int32_t*)(ws + p.idx);
+  T* wts = (T*)(ws + p.wts);
+  int32_t* offsets = (int32_t*)(ws + p.offsets);
+  int32_t* ids = (int32_t*)(ws + p.ids);
+  T* neurons = (T*)(ws + p.neurons);
+  const zaya_taps tz{};
+  const zaya_taps& tp = taps ? *taps : tz;
+  auto tap_copy = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+    return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
+  };
+
+  // cache lengths on the device
+  const int32_t* cl_dev;
+  bool any_cached = false;
+  if (cache) {
+    for (int b = 0; b < B; ++b) any_cached |= cache->cache_len[b] > 0;
+    if (cache->cache_len_dev) {
+      cl_dev = cache->cache_len_dev;
+    } else {
+      HIPCHK(hipMemcpyAsync(ws + p.cache_len, cache->cache_len, (size_t)B * 4, hipMemcpyHostToDevice, st));
+      cl_dev = (const int32_t*)(ws + p.cache_len);
+    }
+  } else {
+    HIPCHK(launch_fill_i32((int32_t*)(ws + p.cache_len), B, 0, st));
+    cl_dev = (const int32_t*)(ws + p.cache_len);
+  }
+  T* Kc = cache ? (T*)cache->K : (T*)(ws + p.Kw);
+  T* Vc = cache ? (T*)cache->V : (T*)(ws + p.Vw);
+  const int cap = cache ? cache->cap : S;
+  T* conv_state = cache ? (T*)cache->conv_state : (T*)(ws + p.convw);
+  T* prev_hs = cache ? (T*)cache->prev_hs : (T*)(ws + p.prevw);
+
+  // a1: input RMSNorm
+  HIPCHK(launch_rmsnorm_stream<T>(x, W(w->ln1_g), xn, T_, H, c->rms_eps, st));
+  HIPCHK(tap_copy(tp.attention_norm_output, xn, (size_t)T_ * H * A));
+  // a2: q/k/v projections (+ the delayed value of the token before this call)
+  HIPCHK(launch_gemm_store<T>(xn, H, W(w->W_qkv), H, T_, QR, H, P, QR, st));
+  const T* Wvd = W(w->W_qkv) + (size_t)(nh * d + nkv * d + nkv * d / 2) * H;
+  if (any_cached) HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, st));
+  // a3: convolution, residual, QK norm, temperature, rotary, value halves, state
+  CcaArgs<T> ca{P, QR, vdp, W(w->conv_w), W(w->conv_b), W(w->temp), conv_state, prev_hs, xn, cl_dev, Q, Kc, Vc, cap,
+                (T*)tp.attention_queries, (T*)tp.attention_keys, (T*)tp.attention_values,
+                B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta};
+  HIPCHK(launch_cca<T>(ca, st));
+  // a4: attention
+  AttnArgs<T> aa{Q, Kc, Vc, O, cl_dev, B, S, nh, nkv, d, cap, c->sliding_window};
+  if (decode)
+    HIPCHK(launch_attn_decode<T>(aa, (float*)(ws + p.part), max_len, st));
+  else
+    HIPCHK(launch_attn_prefill<T>(aa, st));
+  HIPCHK(tap_copy(tp.attention_premix, O, (size_t)T_ * nh * d * A));
+  // a5: o_proj + attention merge
+  HIPCHK(launch_gemm_merge<T>(O, W(w->W_o), T_, H, nh * d, x, W(w->a_hsb), W(w->a_hss), W(w->a_rb), W(w->a_rs), h,
+                              (T*)tp.attention_output, st));
+  HIPCHK(tap_copy(tp.layer_mid, h, (size_t)T_ * H * 4));
+  // a6: post-attention RMSNorm
+  HIPCHK(launch_rmsnorm_stream<T>(h, W(w->ln2_g), hn, T_, H, c->rms_eps, st));
+  HIPCHK(tap_copy(tp.mlp_norm_output, hn, (size_t)T_ * H * A));
+  // a7: router down_proj + carried state
+  HIPCHK(launch_gemm_router_in<T>(hn, W(w->r_Wd), T_, R, H, W(w->r_bd), W(w->r_rss), (const T*)s_in, (T*)s_out, st));
+  // a7/a8: router MLP, selection, skip tokens' merge
+  RouterArgs<T> ra{(const T*)s_out, W(w->r_norm_g), W(w->r_W1), W(w->r_b1), W(w->r_W2), W(w->r_b2), W(w->r_Wout),
+                   w->bal_bias, logits, cls, idx, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb), W(w->m_rs), x_out,
+                   (T*)tp.routed_output, (T*)tp.mlp_output, T_, R, E, H, c->rms_eps};
+  HIPCHK(launch_router<T>(ra, st));
+  HIPCHK(tap_copy(tp.router_logits, logits, (size_t)T_ * (E + 1) * A));
+  HIPCHK(tap_copy(tp.expert_classes, cls, (size_t)T_ * 4));
+  HIPCHK(tap_copy(tp.expert_indices, idx, (size_t)T_ * 4));
+  HIPCHK(tap_copy(tp.expert_weights, wts, (size_t)T_ * A));
+  // a9: buckets
+  HIPCHK(launch_bucket(cls, T_, E, offsets, ids, st));
+  HIPCHK(tap_copy(tp.bucket_offsets, offsets, (size_t)(E + 1) * 4));
+  HIPCHK(tap_copy(tp.bucket_ids, ids, (size_t)T_ * 4));
+  // a10/a11: experts, weighted combine, MoE merge
+  MoeArgs<T> ma{offsets, ids, hn, W(w->W_gu), W(w->W_dn), neurons, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb),
+                W(w->m_rs), x_out, (T*)tp.routed_output, (T*)tp.mlp_output, T_, H, I, E};
+  HIPCHK(launch_moe<T>(ma, st));
+  HIPCHK(tap_copy(tp.mlp_neurons, neurons, (size_t)T_ * I * A));
+  return ZAYA_OK;
+}
+
+size_t block_ws_bytes(const zaya_block_config* c, int B, int S, int decode) { return plan_block(c, B, S, decode).total; }
+
+int block_entry(const zaya_block_config* c, const zaya_block_weights* w, int B, int S, bool decode, const float* x,
+                const void* s_in, float* x_out, void* s_out, const zaya_cca_cache* cache, const zaya_taps* taps,
+                void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_config(c);
+  if (rc) return rc;
+  if ((rc = check_weights(w))) return rc;
+  if (B <= 0 || S <= 0) return fail(ZAYA_EINVAL, "B=%d S=%d must be positive", B, S);
+  if (decode && S != 1) return fail(ZAYA_EINVAL, "decode needs S == 1");
+  if (!x || !x_out || !s_out) return fail(ZAYA_EINVAL, "x, x_out and router_state_out are required");
+  if (decode && !cache) return fail(ZAYA_EINVAL, "decode needs a cache");
+  const size_t T_ = (size_t)B * S;
+  const size_t A = act_bytes(c);
+  if (overlap(x, T_ * c->hidden * 4, x_out, T_ * c->hidden * 4)) return fail(ZAYA_EALIAS, "x_out aliases x");
+  if (overlap(s_in, T_ * c->router_hidden * A, s_out, T_ * c->router_hidden * A))
+    return fail(ZAYA_EALIAS, "router_state_out aliases router_state_in");
+  int max_len = S;
+  if (cache) {
+    if (!cache->K || !cache->V || !cache->conv_state || !cache->prev_hs || !cache->cache_len)
+      return fail(ZAYA_EINVAL, "cache has a NULL member");
+    if (cache->cap <= 0) return fail(ZAYA_ECACHE, "cache cap %d", cache->cap);
+    for (int b = 0; b < B; ++b) {
+      const int L0 = cache->cache_len[b];
+      if (L0 < 0 || (long long)L0 + S > cache->cap)
+        return fail(ZAYA_ECACHE, "cache_len[%d] = %d with S = %d exceeds cap %d", b, L0, S, cache->cap);
+      max_len = std::max(max_len, L0 + S);
+    }
+  }
+  const size_t need = block_ws_bytes(c, B, S, decode);
+  if (!ws || ws_bytes < need) return fail(ZAYA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (((uintptr_t)ws) & 255) return fail(ZAYA_EWORKSPACE, "workspace not 256-byte aligned");
+  Plan p = plan_block(c, B, S, decode);
+  hipStream_t st = (hipStream_t)stream;
+  if (c->act_dtype == ZAYA_BF16)
+    return run_block<bf16_t>(c, w, B, S, decode, x, s_in, x_out, s_out, cache, taps, (char*)ws, p, max_len, st);
+  return run_block<float>(c, w, B, S, decode, x, s_in, x_out, s_out, cache, taps, (char*)ws, p, max_len, st);
+}
+
+// Stack workspace: the block workspace, then two fp32 streams, two router states and
+// the final normed stream.
+struct StackPlan {
+  size_t block, x0, x1, s0, s1, xf, total;
+};
+
+StackPlan plan_stack(const zaya_stack_config* c, int B, int S) {
+  StackPlan p{};
+  const size_t T_ = (size_t)B * S;
+  const size_t A = act_bytes(&c->block);
+  p.block = 0;
+  size_t o = align256(block_ws_bytes(&c->block, B, S, 0));
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  p.x0 = take(T_ * c->block.hidden * 4);
+  p.x1 = take(T_ * c->block.hidden * 4);
+  p.s0 = take(T_ * c->block.router_hidden * A);
+  p.s1 = take(T_ * c->block.router_hidden * A);
+  p.xf = take(T_ * c->block.hidden * A);
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zaya_block_workspace_bytes(const zaya_block_config* cfg, int B, int S, int decode) {
+  if (check_config(cfg) || B <= 0 || S <= 0 || (decode && S != 1)) return 0;
+  return block_ws_bytes(cfg, B, S, decode);
+}
+
+int zaya_block_prefill(const zaya_block_config* cfg, const zaya_block_weights* w, int B, int S, const float* x,
+                       const void* router_state_in, float* x_out, void* router_state_out, const zaya_cca_cache* cache,
+                       const zaya_taps* taps, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_entry(cfg, w, B, S, false, x, router_state_in, x_out, router_state_out, cache, taps, workspace,
+                     workspace_bytes, stream);
+}
+
+int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w, int B, const float* x,
+                      const void* router_state_in, float* x_out, void* router_state_out, const zaya_cca_cache* cache,
+                      const zaya_taps* taps, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_entry(cfg, w, B, 1, true, x, router_state_in, x_out, router_state_out, cache, taps, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S) {
+  if (!cfg || check_config(&cfg->block) || B <= 0 || S <= 0) return 0;
+  return plan_stack(cfg, B, S).total;
+}
+
+int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w, int B, int S, const int32_t* ids,
+                       void* logits, const zaya_cca_cache* caches, const zaya_taps* taps, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!cfg) return fail(ZAYA_EINVAL, "config is NULL");
+  int rc = check_config(&cfg->block);
+  if (rc) return rc;
+  if (cfg->n_layers <= 0 || cfg->vocab <= 0) return fail(ZAYA_ESHAPE, "n_layers %d vocab %d", cfg->n_layers, cfg->vocab);
+  if (!w || !w->embed || !w->emb_shift || !w->emb_scale || !w->final_g || !w->blocks)
+    return fail(ZAYA_EINVAL, "stack weights incomplete");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if ((rc = check_weights(&w->blocks[l]))) return fail(rc, "block %d: %s", l, g_err.c_str());
+  if (B <= 0 || S <= 0) return fail(ZAYA_EINVAL, "B=%d S=%d must be positive", B, S);
+  if (!ids || !logits) return fail(ZAYA_EINVAL, "ids and logits are required");
+  if (caches) {
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const zaya_cca_cache& cc = caches[l];
+      if (!cc.K || !cc.V || !cc.conv_state || !cc.prev_hs || !cc.cache_len)
+        return fail(ZAYA_EINVAL, "cache of block %d has a NULL member", l);
+      for (int b = 0; b < B; ++b)
+        if (cc.cache_len[b] < 0 || (long long)cc.cache_len[b] + S > cc.cap)
+          return fail(ZAYA_ECACHE, "block %d: cache_len[%d] = %d with S = %d exceeds cap %d", l, b, cc.cache_len[b],
+                      S, cc.cap);
+    }
+  }
+  StackPlan p = plan_stack(cfg, B, S);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(ZAYA_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, p.total);
+  if (((uintptr_t)workspace) & 255) return fail(ZAYA_EWORKSPACE, "workspace not 256-byte aligned");
+  const zaya_block_config* c = &cfg->block;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int T_ = B * S, H = c->hidden;
+  float* xs[2] = {(float*)(ws + p.x0), (float*)(ws + p.x1)};
+  void* ss[2] = {ws + p.s0, ws + p.s1};
+  const bool bf = c->act_dtype == ZAYA_BF16;
+  hipError_t e = bf ? launch_embed<bf16_t>(ids, (const bf16_t*)w->embed, (const bf16_t*)w->emb_shift,
+                                           (const bf16_t*)w->emb_scale, xs[0], nullptr, T_, H, cfg->vocab, st)
+                    : launch_embed<float>(ids, (const float*)w->embed, (const float*)w->emb_shift,
+                                          (const float*)w->emb_scale, xs[0], nullptr, T_, H, cfg->vocab, st);
+  if (e != hipSuccess) return fail(ZAYA_EHIP, "embed: %s", hipGetErrorString(e));
+  const size_t bws = block_ws_bytes(c, B, S, 0);
+  const void* s_in = nullptr;
+  int cur = 0;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const zaya_cca_cache* cc = caches ? &caches[l] : nullptr;
+    const zaya_taps* tt = taps ? &taps[l] : nullptr;
+    rc = block_entry(c, &w->blocks[l], B, S, false, xs[cur], s_in, xs[cur ^ 1], ss[cur], cc, tt, ws, bws, stream);
+    if (rc) return fail(rc, "block %d: %s", l, g_err.c_str());
+    s_in = ss[cur];
+    cur ^= 1;
+  }
+  void* xf = ws + p.xf;
+  if (bf) {
+    e = launch_rmsnorm_stream<bf16_t>(xs[cur], (const bf16_t*)w->final_g, (bf16_t*)xf, T_, H, c->rms_eps, st);
+    if (e == hipSuccess)
+      e = launch_gemm_store<bf16_t>((const bf16_t*)xf, H, (const bf16_t*)w->embed, H, T_, cfg->vocab, H,
+                                    (bf16_t*)logits, cfg->vocab, st);
+  } else {
+    e = launch_rmsnorm_stream<float>(xs[cur], (const float*)w->final_g, (float*)xf, T_, H, c->rms_eps, st);
+    if (e == hipSuccess)
+      e = launch_gemm_store<float>((const float*)xf, H, (const float*)w->embed, H, T_, cfg->vocab, H,
+                                   (float*)logits, cfg->vocab, st);
+  }
+  if (e != hipSuccess) return fail(ZAYA_EHIP, "final norm / lm_head: %s", hipGetErrorString(e));
+  return ZAYA_OK;
+}
+
+const char* zaya_last_error(void) { return g_err.c_str(); }
+
+const char* zaya_status_str(int s) {
+  switch (s) {
+    case ZAYA_OK: return "ZAYA_OK";
+    case ZAYA_EINVAL: return "ZAYA_EINVAL";
+    case ZAYA_ESHAPE: return "ZAYA_ESHAPE";
+    case ZAYA_EDTYPE: return "ZAYA_EDTYPE";
+    case ZAYA_EWORKSPACE: return "ZAYA_EWORKSPACE";
+    case ZAYA_ECACHE: return "ZAYA_ECACHE";
+    case ZAYA_EALIAS: return "ZAYA_EALIAS";
+    case ZAYA_EHIP: return "ZAYA_EHIP";
+    default: return "ZAYA_UNKNOWN";
+  }
+}
+
+int zaya_abi_version(void) { return ZAYA_ABI_VERSION; }
+
+}  // extern "C"

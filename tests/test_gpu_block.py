@@ -1,0 +1,76 @@
+"""GPU parity: the HIP block path against the CPU oracle, tap by tap, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from zaya_synth import CONFIGS
+from tests.zaya_harness import BlockRun, check_routing_exact, check_taps, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def small_bf16(**kw):
+    """Full ZAYA1 widths, short sequences: several tiles plus a ragged tail everywhere."""
+    base = dict(name="small", batch=2, seq=200)
+    base.update(kw)
+    return CONFIGS["prefill"].replace(**base)
+
+
+def _full_check(cfg, rows=None, **kw):
+    run = BlockRun(cfg, **kw).run()
+    ref = run.oracle(rows=rows)
+    r = check_routing_exact(run, ref)
+    t = check_taps(run, ref)
+    print(cfg.name, r, {k: (round(v["max"], 6), round(v["rel_rms"], 6)) for k, v in t.items()}, flush=True)
+    return run, ref, r
+
+
+def test_tiny_fp32_block():
+    _full_check(CONFIGS["tiny"])
+
+
+def test_tiny_fp32_skips_and_uneven_experts():
+    _full_check(CONFIGS["tiny"].replace(name="tiny_bb", bal_bias="normal", seq=50, batch=2, conv_std=0.33))
+
+
+def test_bf16_full_width_ragged():
+    _full_check(small_bf16())
+
+
+def test_bf16_block_zero_semantics_and_unit_conv():
+    _full_check(small_bf16(name="small_b0", has_router_state=False, conv_std=0.33, seq=97, batch=1,
+                           gain_std=0.05, bal_bias="normal"))
+
+
+def test_bf16_sliding_window():
+    _full_check(small_bf16(name="small_win", seq=300, batch=1, sliding_window=100))
+
+
+def test_bf16_chunked_prefill_with_cache():
+    _full_check(small_bf16(name="small_cached", seq=77, batch=3, kv_len=130))
+
+
+def test_bf16_decode_small():
+    _full_check(CONFIGS["decode"].replace(name="decode_small", batch=5, kv_len=333))
+
+
+def test_deterministic_rerun():
+    cfg = small_bf16(name="small_det", seq=150)
+    a = BlockRun(cfg).run()
+    out1 = a.x_out.clone()
+    taps1 = {k: v.clone() for k, v in a.taps.items()}
+    a.run()
+    assert torch.equal(out1, a.x_out)
+    for k, v in taps1.items():
+        assert torch.equal(v.view(torch.uint8) if v.dtype != torch.int32 else v,
+                           a.taps[k].view(torch.uint8) if v.dtype != torch.int32 else a.taps[k]), k
+
+
+def test_all_tokens_skip():
+    cfg = CONFIGS["tiny"].replace(name="tiny_skip", seq=40)
+    from zaya_synth import block_weights
+    w = block_weights(cfg)
+    w["bal_bias"][:] = 0
+    w["bal_bias"][cfg.num_experts] = 2.0
+    run, ref, r = _full_check(cfg, w_host=w)
+    assert r["routed"] == 0 and r["skipped"] == cfg.seq

@@ -219,7 +219,7 @@ def block_weights(cfg: ZayaConfig, block: int = 0, seed: int = 0,
     if bal_bias is not None:
         bb = np.asarray(bal_bias, np.float32)
     elif cfg.bal_bias == "normal":
-        bb = normal(seed, n, block, "bal_bias", (E + 1,), 0.0, 0.05)
+        bb = normal(seed, n, block, "bal_bias", (E + 1,), 0.0, 0.01)
     elif cfg.bal_bias == "trained":
         # the pattern the pages report for the trained model: -1 on skip, one expert above 0
         bb = np.zeros(E + 1, np.float32)
