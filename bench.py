@@ -1,0 +1,302 @@
+"""Benchmark of the ZAYA1 block forward on one MI355X.
+
+One step = one zaya_block_prefill call over the full-block prefill workload (bf16,
+batch 1, 4096 tokens, hidden 2048, 8/2 heads of 128, 16 SwiGLU experts of width 2048
+plus skip, router state fed N(0, 1); weights N(0, 0.02); seeded synthetic inputs
+already resident in HBM). ``value`` is prefill tokens/s. The same JSON line also
+carries the decode workload (batch 64, one new token each over an 8192-token cache)
+as ``decode``, the per-stage breakdown measured with HIP events on the launch stream,
+the roofline of the dominant kernel, and the CPU oracle timed on the host as a
+baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_moe_block_amd as Z  # noqa: E402
+from zaya_synth import CONFIGS, block_inputs, block_weights  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+# ----------------------------------------------------------------------------- HIP events via the runtime
+
+class _Hip:
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, ev: int, stream: int):
+        assert self.L.hipEventRecord(ev, stream) == 0
+
+    def elapsed(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev: int):
+        self.L.hipEventDestroy(ev)
+
+
+# ----------------------------------------------------------------------------- setup
+
+class Setup:
+    """Device buffers of one block call (no taps)."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        dev = "cuda"
+        w = block_weights(cfg)
+        self.w = {k: v.to(dev) for k, v in w.items()}
+        inp = block_inputs(cfg)
+        B, S, H, R = cfg.batch, cfg.seq, cfg.hidden_size, cfg.router_hidden
+        self.x = inp["x"].to(dev)
+        self.s_in = inp["s_in"].to(dev)
+        self.x_out = torch.empty((B, S, H), device=dev)
+        self.s_out = torch.empty((B, S, R), device=dev, dtype=cfg.torch_dtype)
+        self.cache = None
+        if cfg.decode:
+            self.cache = {k: inp[k].to(dev) for k in ("K", "V", "conv_state", "prev_hs")}
+            self.cache["cache_len"] = [int(v) for v in inp["cache_len"]]
+            self.cache["cache_len_dev"] = inp["cache_len"].to(dev)
+        self.ws = torch.empty(Z.zaya_block_workspace_bytes(cfg, B, S, cfg.decode), dtype=torch.uint8, device=dev)
+        del w, inp
+
+    def step(self, taps=None):
+        c = self.cfg
+        if c.decode:
+            Z.zaya_block_decode(c, self.w, c.batch, self.x, self.s_in, self.x_out, self.s_out, self.cache, taps,
+                                self.ws)
+        else:
+            Z.zaya_block_prefill(c, self.w, c.batch, c.seq, self.x, self.s_in, self.x_out, self.s_out, self.cache,
+                                 taps, self.ws)
+
+    def routing(self):
+        """Realized routing of this input: (routed tokens, distinct experts used, counts)."""
+        E = self.cfg.num_experts
+        offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        self.step({"bucket_offsets": offs})
+        torch.cuda.synchronize()
+        o = offs.cpu().numpy()
+        counts = np.diff(o)
+        return int(o[-1]), int(np.sum(counts > 0)), counts.tolist()
+
+
+# ----------------------------------------------------------------------------- algorithmic work per stage
+
+def stage_work(cfg, n_routed: int, n_used: int):
+    """(flops, bytes) each stage must do at minimum: every operand read once, every
+    result written once, matmul flops 2*M*N*K, attention flops 4*d per visible
+    (query, key) pair per head; expert weights count only for experts that got tokens."""
+    B, S, H = cfg.batch, cfg.seq, cfg.hidden_size
+    T = B * S
+    nh, nkv, d = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    E, I, R = cfg.num_experts, cfg.moe_intermediate_size, cfg.router_hidden
+    A = 2 if cfg.act_dtype == "bf16" else 4
+    QR = nh * d + 2 * nkv * d
+    L0 = cfg.kv_len
+    W = cfg.sliding_window
+    # visible (query, key) pairs per head per sequence
+    pairs = 0
+    for t in range(S):
+        p = L0 + t
+        lo = max(0, p - W) if W >= 0 else 0
+        pairs += p - lo + 1
+    pairs *= B
+    kv_read = B * nkv * 2 * d * A * (L0 + S) if W < 0 else B * nkv * 2 * d * A * min(L0 + S, W + S)
+    out = {}
+    out["input_norm"] = (0, T * H * 4 + T * H * A + H * A)
+    C = (nh + nkv) * d
+    # with a cache: prev_hs is read for the delayed value of the token before the call
+    out["qkv_proj"] = (2 * T * H * QR + (2 * B * H * nkv * d // 2 if L0 else 0),
+                       T * H * A + QR * H * A + T * QR * A + (B * H * A if L0 else 0))
+    # conv_state read + written, prev_hs written
+    out["cca"] = (0, T * QR * A + T * nh * d * A + 2 * T * nkv * d * A + C * 4 * A + B * (C * 2 * 2 + H) * A)
+    out["attention"] = (4 * d * nh * pairs, T * nh * d * A * 2 + kv_read)
+    out["o_proj_merge"] = (2 * T * nh * d * H, T * nh * d * A + H * nh * d * A + T * H * 4 * 2 + 4 * H * A)
+    out["post_attn_norm"] = (0, T * H * 4 + T * H * A + H * A)
+    out["router_down"] = (2 * T * H * R, T * H * A + R * H * A + 2 * T * R * A)
+    out["router_mlp_select"] = (2 * T * (2 * R * R + (E + 1) * R), T * R * A + 2 * R * R * A + T * (E + 1) * A
+                                + (T - n_routed) * H * 4 * 2)
+    out["buckets"] = (0, T * 4 + n_routed * 4)
+    out["expert_gate_up"] = (2 * n_routed * H * 2 * I, n_used * 2 * I * H * A + n_routed * H * A + n_routed * I * A)
+    out["expert_down_merge"] = (2 * n_routed * I * H, n_used * H * I * A + n_routed * I * A + n_routed * H * 4 * 2)
+    return out
+
+
+def roofline(flops, nbytes, ms):
+    """Bound by whichever roof the kernel's own work hits first; achieved rate on it."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        a = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    a = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4)}
+
+
+# ----------------------------------------------------------------------------- timing
+
+def time_steps(setup: Setup, steps: int, warmup: int, hip: _Hip):
+    for _ in range(warmup):
+        setup.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    t0 = time.perf_counter()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        setup.step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = hip.elapsed(e0, e1) / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return ms, wall
+
+
+def time_stages(setup: Setup, steps: int, hip: _Hip):
+    """Per-stage durations (ms, averaged over steps) from events recorded by the library
+    on the launch stream between its kernels."""
+    n = Z.N_STAGES + 1
+    evs = [[hip.event() for _ in range(n)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        Z.zaya_set_stage_events(evs[k])
+        setup.step()
+    Z.zaya_set_stage_events(None)
+    torch.cuda.synchronize()
+    acc = np.zeros(Z.N_STAGES)
+    for k in range(steps):
+        for s in range(Z.N_STAGES):
+            acc[s] += hip.elapsed(evs[k][s], evs[k][s + 1])
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    return {Z.zaya_stage_name(s): acc[s] / steps for s in range(Z.N_STAGES)}
+
+
+def measure(cfg, steps, warmup, hip):
+    setup = Setup(cfg)
+    n_routed, n_used, counts = setup.routing()
+    ms, wall = time_steps(setup, steps, warmup, hip)
+    stages = time_stages(setup, steps, hip)
+    work = stage_work(cfg, n_routed, n_used)
+    table = {}
+    for name, t in stages.items():
+        f, b = work[name]
+        r = roofline(f, b, t) if t > 0 and (f or b) else None
+        table[name] = {"ms": round(t, 5), "gflop": round(f / 1e9, 3), "mbytes": round(b / 1e6, 3), "roofline": r}
+    dom = max(stages, key=lambda k: stages[k])
+    f, b = work[dom]
+    roof = roofline(f, b, stages[dom])
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    total_f = sum(v[0] for v in work.values())
+    total_b = sum(v[1] for v in work.values())
+    del setup
+    torch.cuda.empty_cache()
+    return {"ms": ms, "wall": wall, "stages": table, "roofline": roof, "n_routed": n_routed, "experts_used": n_used,
+            "expert_counts": counts, "step_gflop": total_f / 1e9, "step_mbytes": total_b / 1e6}
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(cfg):
+    """The CPU oracle (as it stands) on the same seeded prefill input, timed on the host."""
+    from oracle import zaya_oracle as O
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    w = {k: v.float().numpy() for k, v in block_weights(cfg).items()}
+    inp = block_inputs(cfg)
+    x = inp["x"].numpy().astype(np.float64)
+    s = inp["s_in"].float().numpy()
+    t0 = time.perf_counter()
+    O.block_forward(cfg, w, x, s, None)
+    dt = time.perf_counter() - t0
+    return {"value": round(cfg.tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full prefill of the {cfg.seq}-token workload (batch {cfg.batch}) in {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the block's multi-GPU sharding is a design "
+                                   "note, not built (use --gpus 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    hip = _Hip()
+    torch.cuda.init()
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    pcfg = CONFIGS["prefill"]
+    pre = measure(pcfg, args.steps, args.warmup, hip)
+    print(f"[bench] prefill {pre['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    dec = None
+    if not args.no_decode:
+        dcfg = CONFIGS["decode"]
+        dec = measure(dcfg, args.steps, args.warmup, hip)
+        print(f"[bench] decode {dec['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu else cpu_baseline(pcfg)
+    T = pcfg.tokens
+    value = T / (pre["ms"] * 1e-3)
+    line = {
+        "metric": "ZAYA1 block prefill tokens/s + decode tokens/s @bs64, % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": "ZAYA1 block prefill, bf16, batch 1, seq 4096, hidden 2048, 8q/2kv heads x 128, "
+                               "16 experts x 2048 + skip, full causal", "global_batch": pcfg.batch,
+                   "seq_len": pcfg.seq, "parallelism": "single GPU"},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "prefill": {"tok_s": round(value, 1), "step_gflop": round(pre["step_gflop"], 2),
+                    "frac_of_mfma_peak": round(pre["step_gflop"] / (pre["ms"] * 1e-3) / 1e3 / PEAK_BF16_TFLOPS, 4),
+                    "routed_tokens": pre["n_routed"], "experts_used": pre["experts_used"], "stages": pre["stages"],
+                    "wall_s": round(pre["wall"], 4)},
+    }
+    if dec is not None:
+        dcfg = CONFIGS["decode"]
+        line["decode"] = {"tok_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "ms_per_step": round(dec["ms"], 5),
+                          "step_mbytes": round(dec["step_mbytes"], 1),
+                          "frac_of_hbm_peak": round(dec["step_mbytes"] / (dec["ms"] * 1e-3) / 1e3 / PEAK_HBM_GBS, 4),
+                          "experts_used": dec["experts_used"], "roofline": dec["roofline"], "stages": dec["stages"]}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,8 @@
  *  - Pointers named *_dev or documented as device point to device memory of the
  *    current HIP device; host pointers are documented as such.
  *  - All memory is owned by the caller. The library allocates nothing, keeps no
- *    global state and is re-entrant; each call enqueues work on `stream` (a
+ *    global state (apart from the per-thread benchmark hook zaya_set_stage_events)
+ *    and is re-entrant; each call enqueues work on `stream` (a
  *    hipStream_t passed as void*; NULL = the null stream) and returns without
  *    waiting for it.
  *  - Every check happens on the host before the first launch: on any error nothing
@@ -55,8 +56,8 @@ enum zaya_status {
 
 /* Block shape ("Config" and "Printout" on the nnterp page). Supported: head_dim in
  * {64, 128}; n_heads % n_kv_heads == 0 with n_heads / n_kv_heads in {1, 2, 4, 8};
- * rope_dim even and <= head_dim; conv_k == 3; n_experts + 1 <= 64; hidden,
- * expert_inter and router_hidden multiples of 64; router_hidden == 256. */
+ * rope_dim even and <= head_dim; conv_k == 3; n_experts + 1 <= 64; hidden a multiple
+ * of 256 and <= 4096; expert_inter a multiple of 64; router_hidden == 256. */
 typedef struct zaya_block_config {
   int hidden;          /* H (hidden_size) */
   int n_heads;         /* query heads (num_attention_heads) */
@@ -217,6 +218,21 @@ size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S);
 int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w, int B, int S,
                        const int32_t* ids, void* logits, const zaya_cca_cache* caches, const zaya_taps* taps,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Benchmark instrumentation (not needed for correct use). The block forward runs as
+ * ZAYA_N_STAGES stages in this order: input norm, q/k/v projection, CCA projection,
+ * attention, o_proj + merge, post-attention norm, router down_proj, router MLP +
+ * selection, buckets, expert gate/up, expert down + merge. events: host array of
+ * ZAYA_N_STAGES + 1 hipEvent_t handles (passed as void*) created by the caller. While
+ * set (per calling thread), each zaya_block_prefill / zaya_block_decode records
+ * events[k] on its stream right before stage k and events[ZAYA_N_STAGES] after the
+ * last one, so hipEventElapsedTime(events[k], events[k+1]) is stage k's duration.
+ * n == 0 or events == NULL switches recording off. Returns ZAYA_EINVAL if n is neither
+ * 0 nor ZAYA_N_STAGES + 1. The array is copied; the events must outlive the calls. */
+#define ZAYA_N_STAGES 11
+int zaya_set_stage_events(void* const* events, int n);
+/* Name of stage k (0 <= k < ZAYA_N_STAGES), or "" out of range. */
+const char* zaya_stage_name(int k);
 
 /* Message of the calling thread's last failed call ("" if none). */
 const char* zaya_last_error(void);

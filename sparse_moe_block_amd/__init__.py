@@ -100,6 +100,10 @@ def lib():
         L.zaya_status_str.argtypes = [i]
         L.zaya_status_str.restype = C.c_char_p
         L.zaya_abi_version.restype = i
+        L.zaya_set_stage_events.argtypes = [C.POINTER(C.c_void_p), i]
+        L.zaya_set_stage_events.restype = i
+        L.zaya_stage_name.argtypes = [i]
+        L.zaya_stage_name.restype = C.c_char_p
         _lib = L
     return _lib
 
@@ -231,10 +235,27 @@ def zaya_stack_forward(cfg, sw: Mapping, blocks: Sequence[Mapping], B: int, S: i
     _check(rc)
 
 
+N_STAGES = 11
+
+
+def zaya_set_stage_events(events: Optional[Sequence[int]]) -> None:
+    """Record the given hipEvent_t handles (N_STAGES + 1 of them) around each stage of the
+    block calls made by this thread; None switches recording off."""
+    if not events:
+        _check(lib().zaya_set_stage_events(None, 0))
+        return
+    arr = (C.c_void_p * len(events))(*events)
+    _check(lib().zaya_set_stage_events(arr, len(events)))
+
+
+def zaya_stage_name(k: int) -> str:
+    return lib().zaya_stage_name(k).decode()
+
+
 def abi_version() -> int:
     return int(lib().zaya_abi_version())
 
 
 __all__ = ["zaya_block_prefill", "zaya_block_decode", "zaya_stack_forward", "zaya_block_workspace_bytes",
            "zaya_stack_workspace_bytes", "ZayaError", "ZayaLibraryMissing", "lib", "abi_version", "LIB_PATH",
-           "TAP_FIELDS", "WEIGHT_FIELDS"]
+           "TAP_FIELDS", "WEIGHT_FIELDS", "zaya_set_stage_events", "zaya_stage_name", "N_STAGES"]

@@ -121,7 +121,9 @@ struct MoeArgs {
   int ntok, H, I, E;
 };
 template <typename T>
-hipError_t launch_moe(const MoeArgs<T>& a, hipStream_t s);
+hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s);
+template <typename T>
+hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s);
 
 // ---- small helpers
 hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s);

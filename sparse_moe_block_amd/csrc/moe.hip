@@ -184,11 +184,15 @@ __global__ __launch_bounds__(WM* WN * 64) void moe_down_kernel(MoeArgs<T> a) {
 }
 
 template <typename T, int BM, int WM, int WN>
-static hipError_t launch_moe_cfg(const MoeArgs<T>& a, hipStream_t s) {
+static hipError_t launch_gateup_cfg(const MoeArgs<T>& a, hipStream_t s) {
   const int slots = (a.ntok + BM - 1) / BM + a.E;
   hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN>), dim3(a.I / 64, slots), dim3(WM * WN * 64), 0, s, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+template <typename T, int BM, int WM, int WN>
+static hipError_t launch_down_cfg(const MoeArgs<T>& a, hipStream_t s) {
+  const int slots = (a.ntok + BM - 1) / BM + a.E;
   hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN>), dim3(a.H / 128, slots), dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -196,13 +200,22 @@ static hipError_t launch_moe_cfg(const MoeArgs<T>& a, hipStream_t s) {
 // Row tile by load: 16-row tiles when experts see only a few tokens each (decode),
 // 128-row tiles otherwise.
 template <typename T>
-hipError_t launch_moe(const MoeArgs<T>& a, hipStream_t s) {
+hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
-  if (a.ntok <= 32 * a.E) return launch_moe_cfg<T, 16, 1, 4>(a, s);
-  return launch_moe_cfg<T, 128, 2, 2>(a, s);
+  if (a.ntok <= 32 * a.E) return launch_gateup_cfg<T, 16, 1, 4>(a, s);
+  return launch_gateup_cfg<T, 128, 2, 2>(a, s);
 }
 
-template hipError_t launch_moe<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);
-template hipError_t launch_moe<float>(const MoeArgs<float>&, hipStream_t);
+template <typename T>
+hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
+  if (a.ntok <= 0) return hipSuccess;
+  if (a.ntok <= 32 * a.E) return launch_down_cfg<T, 16, 1, 4>(a, s);
+  return launch_down_cfg<T, 128, 2, 2>(a, s);
+}
+
+template hipError_t launch_moe_gateup<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);
+template hipError_t launch_moe_gateup<float>(const MoeArgs<float>&, hipStream_t);
+template hipError_t launch_moe_down<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);
+template hipError_t launch_moe_down<float>(const MoeArgs<float>&, hipStream_t);
 
 }  // namespace zaya

@@ -17,6 +17,11 @@ using namespace zaya;
 namespace {
 
 thread_local std::string g_err;
+thread_local std::vector<hipEvent_t> g_stage_events;  // empty: no stage recording
+
+const char* const kStageNames[ZAYA_N_STAGES] = {
+    "input_norm", "qkv_proj", "cca", "attention", "o_proj_merge", "post_attn_norm",
+    "router_down", "router_mlp_select", "buckets", "expert_gate_up", "expert_down_merge"};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -152,6 +157,10 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
     return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
   };
 
+  auto mark = [&](int k) -> hipError_t {
+    return g_stage_events.empty() ? hipSuccess : hipEventRecord(g_stage_events[k], st);
+  };
+
   // cache lengths on the device
   const int32_t* cl_dev;
   bool any_cached = false;
@@ -174,18 +183,22 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   T* prev_hs = cache ? (T*)cache->prev_hs : (T*)(ws + p.prevw);
 
   // a1: input RMSNorm
+  HIPCHK(mark(0));
   HIPCHK(launch_rmsnorm_stream<T>(x, W(w->ln1_g), xn, T_, H, c->rms_eps, st));
   HIPCHK(tap_copy(tp.attention_norm_output, xn, (size_t)T_ * H * A));
   // a2: q/k/v projections (+ the delayed value of the token before this call)
+  HIPCHK(mark(1));
   HIPCHK(launch_gemm_store<T>(xn, H, W(w->W_qkv), H, T_, QR, H, P, QR, st));
   const T* Wvd = W(w->W_qkv) + (size_t)(nh * d + nkv * d + nkv * d / 2) * H;
   if (any_cached) HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, st));
   // a3: convolution, residual, QK norm, temperature, rotary, value halves, state
+  HIPCHK(mark(2));
   CcaArgs<T> ca{P, QR, vdp, W(w->conv_w), W(w->conv_b), W(w->temp), conv_state, prev_hs, xn, cl_dev, Q, Kc, Vc, cap,
                 (T*)tp.attention_queries, (T*)tp.attention_keys, (T*)tp.attention_values,
                 B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta};
   HIPCHK(launch_cca<T>(ca, st));
   // a4: attention
+  HIPCHK(mark(3));
   AttnArgs<T> aa{Q, Kc, Vc, O, cl_dev, B, S, nh, nkv, d, cap, c->sliding_window};
   if (decode)
     HIPCHK(launch_attn_decode<T>(aa, (float*)(ws + p.part), max_len, st));
@@ -193,15 +206,19 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
     HIPCHK(launch_attn_prefill<T>(aa, st));
   HIPCHK(tap_copy(tp.attention_premix, O, (size_t)T_ * nh * d * A));
   // a5: o_proj + attention merge
+  HIPCHK(mark(4));
   HIPCHK(launch_gemm_merge<T>(O, W(w->W_o), T_, H, nh * d, x, W(w->a_hsb), W(w->a_hss), W(w->a_rb), W(w->a_rs), h,
                               (T*)tp.attention_output, st));
   HIPCHK(tap_copy(tp.layer_mid, h, (size_t)T_ * H * 4));
   // a6: post-attention RMSNorm
+  HIPCHK(mark(5));
   HIPCHK(launch_rmsnorm_stream<T>(h, W(w->ln2_g), hn, T_, H, c->rms_eps, st));
   HIPCHK(tap_copy(tp.mlp_norm_output, hn, (size_t)T_ * H * A));
   // a7: router down_proj + carried state
+  HIPCHK(mark(6));
   HIPCHK(launch_gemm_router_in<T>(hn, W(w->r_Wd), T_, R, H, W(w->r_bd), W(w->r_rss), (const T*)s_in, (T*)s_out, st));
   // a7/a8: router MLP, selection, skip tokens' merge
+  HIPCHK(mark(7));
   RouterArgs<T> ra{(const T*)s_out, W(w->r_norm_g), W(w->r_W1), W(w->r_b1), W(w->r_W2), W(w->r_b2), W(w->r_Wout),
                    w->bal_bias, logits, cls, idx, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb), W(w->m_rs), x_out,
                    (T*)tp.routed_output, (T*)tp.mlp_output, T_, R, E, H, c->rms_eps};
@@ -211,13 +228,18 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(tap_copy(tp.expert_indices, idx, (size_t)T_ * 4));
   HIPCHK(tap_copy(tp.expert_weights, wts, (size_t)T_ * A));
   // a9: buckets
+  HIPCHK(mark(8));
   HIPCHK(launch_bucket(cls, T_, E, offsets, ids, st));
   HIPCHK(tap_copy(tp.bucket_offsets, offsets, (size_t)(E + 1) * 4));
   HIPCHK(tap_copy(tp.bucket_ids, ids, (size_t)T_ * 4));
   // a10/a11: experts, weighted combine, MoE merge
   MoeArgs<T> ma{offsets, ids, hn, W(w->W_gu), W(w->W_dn), neurons, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb),
                 W(w->m_rs), x_out, (T*)tp.routed_output, (T*)tp.mlp_output, T_, H, I, E};
-  HIPCHK(launch_moe<T>(ma, st));
+  HIPCHK(mark(9));
+  HIPCHK(launch_moe_gateup<T>(ma, st));
+  HIPCHK(mark(10));
+  HIPCHK(launch_moe_down<T>(ma, st));
+  HIPCHK(mark(11));
   HIPCHK(tap_copy(tp.mlp_neurons, neurons, (size_t)T_ * I * A));
   return ZAYA_OK;
 }
@@ -383,6 +405,18 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
   if (e != hipSuccess) return fail(ZAYA_EHIP, "final norm / lm_head: %s", hipGetErrorString(e));
   return ZAYA_OK;
 }
+
+int zaya_set_stage_events(void* const* events, int n) {
+  if (n == 0 || events == nullptr) {
+    g_stage_events.clear();
+    return ZAYA_OK;
+  }
+  if (n != ZAYA_N_STAGES + 1) return fail(ZAYA_EINVAL, "need %d events, got %d", ZAYA_N_STAGES + 1, n);
+  g_stage_events.assign((hipEvent_t const*)events, (hipEvent_t const*)events + n);
+  return ZAYA_OK;
+}
+
+const char* zaya_stage_name(int k) { return (k >= 0 && k < ZAYA_N_STAGES) ? kStageNames[k] : ""; }
 
 const char* zaya_last_error(void) { return g_err.c_str(); }
 
