@@ -25,6 +25,7 @@
 namespace zaya {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPrefillChunkTiles = 16;  // longest run of 64-key tiles one prefill unit handles
 
 // ----------------------------------------------------------------------------- prefill
 
@@ -136,27 +137,55 @@ __device__ __forceinline__ typename Mfma<T>::frag load_vt_frag(const char* vt, i
   return f;
 }
 
+// Key-tile range of query tile qblk of sequence b, and how it is split into chunks:
+// chunk c of nc covers tiles [kt_begin + c*n/nc, kt_begin + (c+1)*n/nc).
+struct QTile {
+  int q0, nq, qp_min, qp_max, kt_begin, n, nc;
+};
+
+__device__ __forceinline__ QTile qtile(int qblk, int S, int L0, int W, int NC) {
+  QTile r;
+  r.q0 = qblk * 32;
+  r.nq = min(32, S - r.q0);
+  r.qp_min = L0 + r.q0;
+  r.qp_max = L0 + r.q0 + r.nq - 1;
+  const int klo = W >= 0 ? max(0, r.qp_min - W) : 0;
+  r.kt_begin = klo / 64;
+  r.n = r.qp_max / 64 + 1 - r.kt_begin;
+  r.nc = min(NC, r.n);
+  return r;
+}
+
+// One unit = (query tile of 32 tokens, chunk of its key tiles, KV group, sequence).
+// Units are numbered so the latest (heaviest) query tiles come first. A query tile
+// whose keys fit one chunk writes its output directly; otherwise each chunk writes
+// (unnormalised output, running max, running sum) per row for the combine pass.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) void attn_prefill_kernel(
+    AttnArgs<T> a, float* __restrict__ part, int NC) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   using L = AttnLds<T, D>;
   constexpr int NT = 64 * G;
   constexpr int DC = D / 32;  // 32-wide K chunks of the QK product
   constexpr int DB = D / 16;  // 16-row output blocks of O^T
-  __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds[2 * L::kBytes];
 
-  const int nqb = gridDim.x;
-  const int qblk = nqb - 1 - (int)blockIdx.x;  // heavy (late) query tiles first
+  const int nqb = (a.S + 31) / 32;
+  const int c = blockIdx.x % NC;
+  const int qblk = nqb - 1 - (int)(blockIdx.x / NC);
   const int g = blockIdx.y, b = blockIdx.z;
+  const int S = a.S, L0 = a.cache_len[b];
+  const int W = a.window;
+  const QTile qt = qtile(qblk, S, L0, W, NC);
+  if (c >= qt.nc) return;
+  const int kt0 = qt.kt_begin + c * qt.n / qt.nc;
+  const int kt1 = qt.kt_begin + (c + 1) * qt.n / qt.nc;
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = g * G + wave;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int S = a.S, L0 = a.cache_len[b];
-  const int q0 = qblk * 32;
-  const int nq = min(32, S - q0);
-  const int qp_min = L0 + q0, qp_max = L0 + q0 + nq - 1;
-  const int W = a.window;
+  const int q0 = qt.q0, qp_min = qt.qp_min, qp_max = qt.qp_max;
 
   // queries of this head: rows q0 + qb*16 + r16
   frag qf[2][DC];
@@ -176,8 +205,6 @@ __global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
-  const int klo = W >= 0 ? max(0, qp_min - W) : 0;
-  const int kt_begin = klo / 64, kt_end = qp_max / 64 + 1;
   const int kvalid = L0 + S;
   const T* Kb = a.K + ((size_t)b * a.nkv + g) * a.cap * D;
   const T* Vb = a.V + ((size_t)b * a.nkv + g) * a.cap * D;
@@ -188,13 +215,15 @@ __global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
   constexpr int VT = (TR::kVTasks + NT - 1) / NT;
   constexpr int VW = 8 * (int)sizeof(T) / 16;
   uint4 kr[KC], vr[VT * 4 * VW];
-  attn_load_tile<T, D, NT>(Kb, Vb, kt_begin * 64, kvalid, kr, vr);
+  attn_load_tile<T, D, NT>(Kb, Vb, kt0 * 64, kvalid, kr, vr);
+  attn_store_tile<T, D, NT>(lds, kr, vr);
+  __syncthreads();
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    __syncthreads();  // previous tile fully consumed
-    attn_store_tile<T, D, NT>(lds, kr, vr);
-    __syncthreads();
-    if (kt + 1 < kt_end) attn_load_tile<T, D, NT>(Kb, Vb, (kt + 1) * 64, kvalid, kr, vr);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) attn_load_tile<T, D, NT>(Kb, Vb, (kt + 1) * 64, kvalid, kr, vr);
+    const char* kbuf = lds + cur * L::kBytes;
     const int k0 = kt * 64;
 
     // S^T = K Q^T: s[qb][kb] holds S[q = qb*16 + r16][key = k0 + kb*16 + 4*grp + i]
@@ -207,7 +236,7 @@ __global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const frag kf = MF::load(reinterpret_cast<const T*>(lds + (kb * 16 + r16) * L::kKRow) + dc * 32 + grp * 8);
+        const frag kf = MF::load(reinterpret_cast<const T*>(kbuf + (kb * 16 + r16) * L::kKRow) + dc * 32 + grp * 8);
         s[0][kb] = MF::mma(kf, qf[0][dc], s[0][kb]);
         s[1][kb] = MF::mma(kf, qf[1][dc], s[1][kb]);
       }
@@ -233,13 +262,13 @@ __global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run[qb], mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[qb] - m_use);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = exp2f(s[qb][kb][i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(s[qb][kb][i] - m_use);
           s[qb][kb][i] = pv;
           ps += pv;
         }
@@ -252,41 +281,111 @@ __global__ __launch_bounds__(64 * G) void attn_prefill_kernel(AttnArgs<T> a) {
     }
 
     // O^T += V^T P^T over two 32-key chunks
-    const char* vt = lds + L::kKBytes;
+    const char* vt = kbuf + L::kKBytes;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int cc = 0; cc < 2; ++cc) {
       frag pf[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float pv[8] = {s[qb][2 * c][0],     s[qb][2 * c][1],     s[qb][2 * c][2],     s[qb][2 * c][3],
-                             s[qb][2 * c + 1][0], s[qb][2 * c + 1][1], s[qb][2 * c + 1][2], s[qb][2 * c + 1][3]};
+        const float pv[8] = {s[qb][2 * cc][0],     s[qb][2 * cc][1],     s[qb][2 * cc][2],     s[qb][2 * cc][3],
+                             s[qb][2 * cc + 1][0], s[qb][2 * cc + 1][1], s[qb][2 * cc + 1][2], s[qb][2 * cc + 1][3]};
         pf[qb] = MF::pack(pv);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const frag vf = load_vt_frag<T, D>(vt, db * 16 + r16, c, grp);
+        const frag vf = load_vt_frag<T, D>(vt, db * 16 + r16, cc, grp);
         o[0][db] = MF::mma(vf, pf[0], o[0][db]);
         o[1][db] = MF::mma(vf, pf[1], o[1][db]);
       }
     }
+    if (more) attn_store_tile<T, D, NT>(lds + (cur ^ 1) * L::kBytes, kr, vr);
+    __syncthreads();
   }
 
-  // finalize: O[q][d] /= row sum; lane holds d = db*16 + 4*grp + i of query r16
+  // lane holds O[q = qb*16 + r16][d = db*16 + 4*grp + i]; the row sum is spread over
+  // the four lanes of the row
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float l = l_run[qb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int t = q0 + qb * 16 + r16;
-    if (t < S) {
-      T* orow = a.O + (((size_t)b * S + t) * a.nh + h) * D;
+    const int row = qb * 16 + r16;
+    const int t = q0 + row;
+    if (qt.nc == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      if (t < S) {
+        T* orow = a.O + (((size_t)b * S + t) * a.nh + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          float v[4] = {o[qb][db][0] * inv, o[qb][db][1] * inv, o[qb][db][2] * inv, o[qb][db][3] * inv};
+          store4(orow + db * 16 + 4 * grp, v);
+        }
+      }
+    } else {
+      float* pr = part + (((((size_t)b * a.nkv + g) * nqb + qblk) * NC + c) * G + wave) * 32 * (D + 2) +
+                  (size_t)row * (D + 2);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        float v[4] = {o[qb][db][0] * inv, o[qb][db][1] * inv, o[qb][db][2] * inv, o[qb][db][3] * inv};
-        store4(orow + db * 16 + 4 * grp, v);
+        float v[4] = {o[qb][db][0], o[qb][db][1], o[qb][db][2], o[qb][db][3]};
+        store4(pr + db * 16 + 4 * grp, v);
+      }
+      if (grp == 0) {
+        pr[D] = m_run[qb];
+        pr[D + 1] = l;
       }
     }
+  }
+}
+
+// Merge the chunks of every split query tile: O = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
+// One wave per head; lane pair (2r, 2r+1) owns row r, each lane half of its dims, so
+// every load of the pass is independent of the others.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * G) void attn_prefill_combine_kernel(AttnArgs<T> a, const float* __restrict__ part,
+                                                                       int NC) {
+  const int nqb = (a.S + 31) / 32;
+  const int qblk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L0 = a.cache_len[b];
+  const QTile qt = qtile(qblk, a.S, L0, a.window, NC);
+  if (qt.nc == 1) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = g * G + wave;
+  const int row = lane >> 1, half = lane & 1;
+  if (row >= qt.nq) return;
+  const size_t unit0 = (((size_t)b * a.nkv + g) * nqb + qblk) * NC;
+  const size_t ustride = (size_t)G * 32 * (D + 2);
+  const float* base = part + (unit0 * G + wave) * 32 * (D + 2) + (size_t)row * (D + 2);
+  float mc[16];
+  float M = -INFINITY;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    mc[cc] = cc < qt.nc ? base[cc * ustride + D] : -INFINITY;
+    M = fmaxf(M, mc[cc]);
+  }
+  float lsum = 0.f;
+  float acc[D / 2];
+#pragma unroll
+  for (int j = 0; j < D / 2; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    if (cc >= qt.nc) break;
+    const float sc = mc[cc] == -INFINITY ? 0.f : exp2f(mc[cc] - M);
+    const float* pr = base + cc * ustride + half * (D / 2);
+    lsum += sc * base[cc * ustride + D + 1];
+#pragma unroll
+    for (int j = 0; j < D / 2; j += 4) {
+      float v[4];
+      load4(pr + j, v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j + i] += sc * v[i];
+    }
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  T* orow = a.O + (((size_t)b * a.S + qt.q0 + row) * a.nh + h) * D + half * (D / 2);
+#pragma unroll
+  for (int j = 0; j < D / 2; j += 4) {
+    float v[4] = {acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv};
+    store4(orow + j, v);
   }
 }
 
@@ -300,12 +399,12 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
                                                              int chunk) {
   constexpr int NT = 64 * G;
   constexpr int KROW = D * (int)sizeof(T) + 16;
-  constexpr int VROW = D * (int)sizeof(T);
+  constexpr int VROW = D * (int)sizeof(T) + 16;
   constexpr int DPL = D / 64;  // dims per lane in the weighted sum
   __shared__ __attribute__((aligned(16))) char kt_s[64 * KROW];
   __shared__ __attribute__((aligned(16))) char vt_s[64 * VROW];
-  __shared__ float q_s[G][D];
-  __shared__ float p_s[G][64];
+  __shared__ __attribute__((aligned(16))) float q_s[G][D];
+  __shared__ __attribute__((aligned(16))) float p_s[G][64];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -331,8 +430,8 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   constexpr int CPR = D / E16;               // 16-byte chunks per row
   constexpr int NCH = 64 * CPR;              // per tile, per tensor
   constexpr int PER = (NCH + NT - 1) / NT;
-  for (int t0 = (c_lo / 64) * 64; t0 < c_hi; t0 += 64) {
-    uint4 kr[PER], vr[PER];
+  uint4 kr[PER], vr[PER];
+  auto load = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int ch = threadIdx.x + i * NT;
@@ -341,6 +440,10 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
       kr[i] = ok ? *reinterpret_cast<const uint4*>(Kb + (size_t)(t0 + key) * D + col) : make_uint4(0, 0, 0, 0);
       vr[i] = ok ? *reinterpret_cast<const uint4*>(Vb + (size_t)(t0 + key) * D + col) : make_uint4(0, 0, 0, 0);
     }
+  };
+  const int t_first = (c_lo / 64) * 64;
+  if (t_first < c_hi) load(t_first);
+  for (int t0 = t_first; t0 < c_hi; t0 += 64) {
     __syncthreads();  // previous tile consumed (and q_s written on the first pass)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -352,34 +455,47 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
       }
     }
     __syncthreads();
+    if (t0 + 64 < c_hi) load(t0 + 64);  // next tile in flight during this one
     // scores: lane = key
     const int kp = t0 + lane;
     const T* krow = reinterpret_cast<const T*>(kt_s + lane * KROW);
-    float acc = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < D; i += 4) {
-      float kv[4];
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; i += 8) {
+      float kv[8];
       load4(krow + i, kv);
-      acc += q_s[wave][i] * kv[0] + q_s[wave][i + 1] * kv[1] + q_s[wave][i + 2] * kv[2] + q_s[wave][i + 3] * kv[3];
+      load4(krow + i + 4, kv + 4);
+      const float4 qa = *reinterpret_cast<const float4*>(&q_s[wave][i]);
+      const float4 qb = *reinterpret_cast<const float4*>(&q_s[wave][i + 4]);
+      acc0 += qa.x * kv[0] + qa.y * kv[1] + qa.z * kv[2] + qa.w * kv[3];
+      acc1 += qb.x * kv[4] + qb.y * kv[5] + qb.z * kv[6] + qb.w * kv[7];
     }
     const bool vis = kp >= c_lo && kp < c_hi;
-    const float sv = vis ? acc * sscale : -INFINITY;
+    const float sv = vis ? (acc0 + acc1) * sscale : -INFINITY;
     const float mx = wave_max(sv);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    const float pv = exp2f(sv - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float pv = __builtin_amdgcn_exp2f(sv - m_use);
     l_run = l_run * alpha + pv;
     m_run = m_new;
     p_s[wave][lane] = pv;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int j = 0; j < DPL; ++j) o[j] *= alpha;
-    for (int k = 0; k < 64; ++k) {
-      const float pk = p_s[wave][k];
-      const T* vrow = reinterpret_cast<const T*>(vt_s + k * VROW);
+    // weighted sum: lane owns dims [lane*DPL, lane*DPL + DPL); four keys per step
+#pragma unroll 4
+    for (int k = 0; k < 64; k += 4) {
+      const float4 pk = *reinterpret_cast<const float4*>(&p_s[wave][k]);
+      const float pkk[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) o[j] += pk * Act<T>::tof(vrow[lane * DPL + j]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const T* vrow = reinterpret_cast<const T*>(vt_s + (k + kk) * VROW) + lane * DPL;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[j] += pkk[kk] * Act<T>::tof(vrow[j]);
+      }
     }
   }
   l_run = wave_sum(l_run);
@@ -392,6 +508,8 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   }
 }
 
+// Merge the key chunks of one (sequence, head): each lane owns D/64 dims; the chunk
+// maxima are read in one pass so all loads are independent.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnArgs<T> a, const float* __restrict__ part,
                                                                   int nchunk) {
@@ -400,30 +518,48 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnArgs<T> a, 
   const int g = h / G, w = h % G;
   const float* base = part + (((size_t)b * a.nkv + g) * nchunk * G + w) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, base[c * stride + D]);
-  float lsum = 0.f;
+  __shared__ float m_s[128], sc_s[128];
+  __shared__ float M_s, L_s;
+  for (int c = threadIdx.x; c < nchunk; c += 64) m_s[c] = base[c * stride + D];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, m_s[c]);
+    M_s = M;
+  }
+  __syncthreads();
+  float lpart = 0.f;
+  for (int c = threadIdx.x; c < nchunk; c += 64) {
+    const float sc = m_s[c] == -INFINITY ? 0.f : exp2f(m_s[c] - M_s);
+    sc_s[c] = sc;
+    lpart += sc * base[c * stride + D + 1];
+  }
+  lpart = wave_sum(lpart);
+  if (threadIdx.x == 0) L_s = lpart;
+  __syncthreads();
   float acc[D / 64];
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
+#pragma unroll 4
   for (int c = 0; c < nchunk; ++c) {
-    const float* pc = base + c * stride;
-    const float mc = pc[D];
-    const float sc = mc == -INFINITY ? 0.f : exp2f(mc - M);
-    lsum += sc * pc[D + 1];
+    const float sc = sc_s[c];
+    const float* pc = base + c * stride + threadIdx.x * (D / 64);
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) acc[j] += sc * pc[threadIdx.x * (D / 64) + j];
+    for (int j = 0; j < D / 64; ++j) acc[j] += sc * pc[j];
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float inv = L_s > 0.f ? 1.f / L_s : 0.f;
   T* orow = a.O + ((size_t)b * a.nh + h) * D;
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) orow[threadIdx.x * (D / 64) + j] = Act<T>::cvt(acc[j] * inv);
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_prefill_dg(const AttnArgs<T>& a, hipStream_t s) {
-  dim3 grid((a.S + 31) / 32, a.nkv, a.B);
-  hipLaunchKernelGGL((attn_prefill_kernel<T, D, G>), grid, dim3(64 * G), 0, s, a);
+static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, hipStream_t s) {
+  const int nqb = (a.S + 31) / 32;
+  hipLaunchKernelGGL((attn_prefill_kernel<T, D, G>), dim3(nqb * NC, a.nkv, a.B), dim3(64 * G), 0, s, a, part, NC);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || NC == 1) return e;
+  hipLaunchKernelGGL((attn_prefill_combine_kernel<T, D, G>), dim3(nqb, a.nkv, a.B), dim3(64 * G), 0, s, a, part, NC);
   return hipGetLastError();
 }
 
@@ -458,8 +594,24 @@ static hipError_t launch_decode_dg(const AttnArgs<T>& a, float* part, int maxlen
   } while (0)
 
 template <typename T>
-hipError_t launch_attn_prefill(const AttnArgs<T>& a, hipStream_t s) {
-  ZAYA_DISPATCH_DG(launch_prefill_dg, a, s);
+hipError_t launch_attn_prefill(const AttnArgs<T>& a, float* part, int NC, hipStream_t s) {
+  ZAYA_DISPATCH_DG(launch_prefill_dg, a, part, NC, s);
+}
+
+// Chunks per query tile: enough that no unit exceeds kPrefillChunkTiles key tiles of the
+// longest query tile (capped at 16).
+int attn_prefill_chunks(int S, int max_cache_len, int window) {
+  const int qp_max = max_cache_len + S - 1;
+  const int klo = window >= 0 ? (qp_max - 31 - window > 0 ? qp_max - 31 - window : 0) : 0;
+  const int tiles = qp_max / 64 + 1 - klo / 64;
+  int nc = (tiles + kPrefillChunkTiles - 1) / kPrefillChunkTiles;
+  return nc < 1 ? 1 : (nc > 16 ? 16 : nc);
+}
+
+size_t attn_prefill_part_bytes(int B, int S, int nkv, int G, int d, int NC) {
+  if (NC <= 1) return 0;
+  const size_t nqb = (size_t)(S + 31) / 32;
+  return (size_t)B * nkv * nqb * NC * G * 32 * (d + 2) * sizeof(float);
 }
 
 template <typename T>
@@ -471,8 +623,8 @@ size_t attn_decode_part_bytes(int B, int nkv, int G, int d) {
   return (size_t)B * nkv * kDecChunksMax * G * (d + 2) * sizeof(float);
 }
 
-template hipError_t launch_attn_prefill<bf16_t>(const AttnArgs<bf16_t>&, hipStream_t);
-template hipError_t launch_attn_prefill<float>(const AttnArgs<float>&, hipStream_t);
+template hipError_t launch_attn_prefill<bf16_t>(const AttnArgs<bf16_t>&, float*, int, hipStream_t);
+template hipError_t launch_attn_prefill<float>(const AttnArgs<float>&, float*, int, hipStream_t);
 template hipError_t launch_attn_decode<bf16_t>(const AttnArgs<bf16_t>&, float*, int, hipStream_t);
 template hipError_t launch_attn_decode<float>(const AttnArgs<float>&, float*, int, hipStream_t);
 

@@ -21,6 +21,7 @@ namespace zaya {
 typedef uint16_t bf16_t;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // native 16-byte register quad
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

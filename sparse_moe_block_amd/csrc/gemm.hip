@@ -78,8 +78,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int m0 = (wg / ntn) * BM, n0 = (wg % ntn) * BN;
   Tile t;
-  t.set_a([&](int r) -> const T* { return m0 + r < M ? A + (size_t)(m0 + r) * lda : nullptr; });
-  t.set_b([&](int r) -> const T* { return n0 + r < N ? B + (size_t)(n0 + r) * ldb : nullptr; });
+  t.set_a([&](int r) -> const T* { return A + (size_t)min(m0 + r, M - 1) * lda; });
+  t.set_b([&](int r) -> const T* { return B + (size_t)min(n0 + r, N - 1) * ldb; });
   t.run(smem, K / Tile::kBK);
   t.epilogue([&](int m, int n, const float* v) {
     if (m0 + m < M && n0 + n < N) epi(m0 + m, n0 + n, v);
@@ -94,39 +94,103 @@ static hipError_t launch_cfg(const T* A, int lda, const T* B, int ldb, int M, in
   return hipGetLastError();
 }
 
-// Tile choice: 128x128 (4 waves of 64x64) when there are enough rows, else 32x64
-// (4 waves of 32x16) so weight-streaming GEMMs with few rows still spread over many CUs.
+// Split-K for GEMMs with few rows (decode): each workgroup reduces one K range of a
+// 64 x 64 output tile into fp32 partials; a second pass sums the ranges in a fixed
+// order and applies the epilogue, so results do not depend on scheduling.
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_splitk_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
+                                                          int ldb, int M, int N, int K, int kparts,
+                                                          float* __restrict__ part) {
+  using Tile = GemmTile<T, 64, 64, 2, 2>;
+  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  const int ntn = (N + 63) / 64;
+  const int n0 = (blockIdx.x % ntn) * 64;
+  const int m0 = (blockIdx.x / ntn) * 64;
+  const int kp = blockIdx.y;
+  const int kslices = K / Tile::kBK;
+  const int s0 = kp * kslices / kparts, s1 = (kp + 1) * kslices / kparts;
+  const int koff = s0 * Tile::kBK;
+  Tile t;
+  t.set_a([&](int r) -> const T* { return A + (size_t)min(m0 + r, M - 1) * lda + koff; });
+  t.set_b([&](int r) -> const T* { return B + (size_t)min(n0 + r, N - 1) * ldb + koff; });
+  t.run(smem, s1 - s0);
+  float* pp = part + (size_t)kp * M * N;
+  t.epilogue([&](int m, int n, const float* v) {
+    if (m0 + m < M && n0 + n < N) store4(pp + (size_t)(m0 + m) * N + n0 + n, v);
+  });
+}
+
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ part, int M, int N,
+                                                                 int kparts, Epi epi) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= M * N) return;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int kp = 0; kp < kparts; ++kp) {
+    float w[4];
+    load4(part + (size_t)kp * M * N + i, w);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] += w[c];
+  }
+  epi(i / N, i % N, v);
+}
+
+// Tile choice by grid size: the largest tile that still gives about one workgroup per
+// CU or more; GEMMs with at most 64 rows split K instead (they stream weights).
 template <typename T, class Epi>
-static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, int N, int K, Epi epi, hipStream_t s) {
+static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, int N, int K, Epi epi, float* part,
+                             size_t part_bytes, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (M >= 512) return launch_cfg<T, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
+  constexpr int kBK = 128 / (int)sizeof(T);
+  if (M <= 64 && part) {
+    const int ntiles = (N + 63) / 64;
+    int kparts = 1;
+    while (ntiles * kparts * 2 <= 512 && (K / kBK) / (kparts * 2) >= 4 &&
+           (size_t)M * N * kparts * 2 * sizeof(float) <= part_bytes)
+      kparts *= 2;
+    if (kparts > 1) {
+      hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(ntiles, kparts), dim3(256), 0, s, A, lda, B, ldb, M, N, K, kparts,
+                         part);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(gemm_splitk_reduce_kernel<Epi>, dim3((M * N / 4 + 255) / 256), dim3(256), 0, s, part, M, N,
+                         kparts, epi);
+      return hipGetLastError();
+    }
+  }
+  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
+  if (t128 >= 240) return launch_cfg<T, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
+  if (t64 >= 120) return launch_cfg<T, 64, 64, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
   return launch_cfg<T, 32, 64, 1, 4>(A, lda, B, ldb, M, N, K, epi, s);
 }
 
 template <typename T>
 hipError_t launch_gemm_store(const T* A, int lda, const T* B, int ldb, int M, int N, int K, T* C, int ldc,
-                             hipStream_t s) {
-  return launch_any(A, lda, B, ldb, M, N, K, EpiStore<T>{C, ldc}, s);
+                             float* part, size_t part_bytes, hipStream_t s) {
+  return launch_any(A, lda, B, ldb, M, N, K, EpiStore<T>{C, ldc}, part, part_bytes, s);
 }
 
 template <typename T>
 hipError_t launch_gemm_merge(const T* O, const T* Wo, int M, int H, int K, const float* x, const T* hsb, const T* hss,
-                             const T* rb, const T* rs, float* h, T* a_tap, hipStream_t s) {
-  return launch_any(O, K, Wo, K, M, H, K, EpiMerge<T>{x, hsb, hss, rb, rs, h, a_tap, H}, s);
+                             const T* rb, const T* rs, float* h, T* a_tap, float* part, size_t part_bytes,
+                             hipStream_t s) {
+  return launch_any(O, K, Wo, K, M, H, K, EpiMerge<T>{x, hsb, hss, rb, rs, h, a_tap, H}, part, part_bytes, s);
 }
 
 template <typename T>
 hipError_t launch_gemm_router_in(const T* hn, const T* Wd, int M, int R, int H, const T* b, const T* rss,
-                                 const T* s_in, T* u, hipStream_t s) {
-  return launch_any(hn, H, Wd, H, M, R, H, EpiRouterIn<T>{b, rss, s_in, u, R}, s);
+                                 const T* s_in, T* u, float* part, size_t part_bytes, hipStream_t s) {
+  return launch_any(hn, H, Wd, H, M, R, H, EpiRouterIn<T>{b, rss, s_in, u, R}, part, part_bytes, s);
 }
 
 #define ZAYA_INST(T)                                                                                                 \
-  template hipError_t launch_gemm_store<T>(const T*, int, const T*, int, int, int, int, T*, int, hipStream_t);       \
+  template hipError_t launch_gemm_store<T>(const T*, int, const T*, int, int, int, int, T*, int, float*, size_t,     \
+                                           hipStream_t);                                                             \
   template hipError_t launch_gemm_merge<T>(const T*, const T*, int, int, int, const float*, const T*, const T*,      \
-                                           const T*, const T*, float*, T*, hipStream_t);                             \
+                                           const T*, const T*, float*, T*, float*, size_t, hipStream_t);             \
   template hipError_t launch_gemm_router_in<T>(const T*, const T*, int, int, int, const T*, const T*, const T*, T*, \
-                                               hipStream_t);
+                                               float*, size_t, hipStream_t);
 ZAYA_INST(bf16_t)
 ZAYA_INST(float)
 #undef ZAYA_INST

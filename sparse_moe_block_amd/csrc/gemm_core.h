@@ -2,17 +2,19 @@
 //
 // A workgroup of WM x WN waves computes a BM x BN tile; each wave a (BM/WM) x (BN/WN)
 // sub-tile made of 16x16 MFMA blocks. Tiles of 128-byte K-slices (64 bf16 or 32 fp32)
-// are staged through LDS, double-buffered with register prefetch: the global loads of
-// slice k+1 are in flight while slice k feeds the MFMAs. Rows are padded by 16 bytes
-// in LDS so the 16-byte fragment reads of 16 consecutive rows spread over the banks.
+// are staged through a double-buffered LDS tile, fed from a ring of register stages
+// that keeps the global loads of the next few slices in flight while one slice feeds
+// the MFMAs (a single slice of lookahead leaves every iteration waiting on memory).
+// LDS rows are XOR-swizzled (see swz) so fragment reads and slice writes are free of
+// bank conflicts without padding.
 //
 // Operands are swapped on purpose: the MFMA's first operand takes rows of B (the
 // weights, index n) and its second rows of A (index m), so each lane ends up holding
 // four consecutive n of one m — epilogues then issue 8-/16-byte vector stores.
 //
-// Row sources are given per 16-byte load chunk as byte pointers (NULL = zero row), so
-// the same engine serves dense GEMMs, gathered rows (token buckets) and interleaved
-// weight rows (gate/up pairs).
+// Row sources are given per 16-byte load chunk as byte pointers, so the same engine
+// serves dense GEMMs, gathered rows (token buckets) and interleaved weight rows (gate/up
+// pairs).
 #pragma once
 #include "common.h"
 
@@ -24,14 +26,13 @@ struct GemmTile {
   using frag = typename MF::frag;
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kRowBytes = 128;                    // one K slice of a row
-  static constexpr int kLdsRow = kRowBytes + 16;           // padded LDS row stride
   static constexpr int kBK = kRowBytes / (int)sizeof(T);   // K elements per slice
   static constexpr int kKSteps = kBK / 32;                 // MFMA k-steps per slice
   static constexpr int kTM = BM / (WM * 16);
   static constexpr int kTN = BN / (WN * 16);
   static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;
   static constexpr int kBChunks = (BN * 8 + kThreads - 1) / kThreads;
-  static constexpr int kBufBytes = (BM + BN) * kLdsRow;
+  static constexpr int kBufBytes = (BM + BN) * kRowBytes;
   static constexpr int kLdsBytes = 2 * kBufBytes;
   static_assert(BM % (WM * 16) == 0 && BN % (WN * 16) == 0, "tile must split into 16x16 blocks");
   static_assert(kKSteps >= 1, "slice too short");
@@ -39,6 +40,13 @@ struct GemmTile {
   f32x4 acc[kTM][kTN];
   const char* pa[kAChunks];
   const char* pb[kBChunks];
+
+  // LDS rows are 128 bytes (eight 16-byte chunks) with no padding; chunk j of row r is
+  // stored at position j ^ swz(r). Sixteen consecutive rows read at the same logical
+  // chunk, and eight chunks of one row written by eight lanes, then land on distinct
+  // banks.
+  __device__ __forceinline__ static int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+  __device__ __forceinline__ static int lds_off(int r, int chunk) { return r * kRowBytes + ((chunk ^ swz(r)) << 4); }
 
   __device__ __forceinline__ void zero_acc() {
 #pragma unroll
@@ -49,48 +57,61 @@ struct GemmTile {
 
   // Chunk c of the A tile covers row c / 8, bytes (c % 8) * 16 .. +16 of each K slice.
   __device__ __forceinline__ static int chunk_row(int i) { return (int)(threadIdx.x + i * kThreads) >> 3; }
-  __device__ __forceinline__ static int chunk_col(int i) { return ((int)(threadIdx.x + i * kThreads) & 7) * 16; }
+  __device__ __forceinline__ static int chunk_col(int i) { return ((int)(threadIdx.x + i * kThreads) & 7); }
 
-  // set_a(rowptr): rowptr(r) -> const T* to row r at k = 0 (or NULL for a zero row)
+  // set_a(rowptr): rowptr(r) -> const T* to row r at k = 0, for every r < BM. Rows past
+  // the problem edge must still point at readable memory (callers clamp them to a
+  // valid row); their products land only in outputs the epilogue discards.
   template <class F>
   __device__ __forceinline__ void set_a(F rowptr) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
-      int r = chunk_row(i);
-      const T* p = (r < BM) ? rowptr(r) : nullptr;
-      pa[i] = p ? reinterpret_cast<const char*>(p) + chunk_col(i) : nullptr;
+      const int r = min(chunk_row(i), BM - 1);
+      pa[i] = reinterpret_cast<const char*>(rowptr(r)) + chunk_col(i) * 16;
     }
   }
   template <class F>
   __device__ __forceinline__ void set_b(F rowptr) {
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
-      int r = chunk_row(i);
-      const T* p = (r < BN) ? rowptr(r) : nullptr;
-      pb[i] = p ? reinterpret_cast<const char*>(p) + chunk_col(i) : nullptr;
+      const int r = min(chunk_row(i), BN - 1);
+      pb[i] = reinterpret_cast<const char*>(rowptr(r)) + chunk_col(i) * 16;
     }
   }
 
-  __device__ __forceinline__ void load_slice(int kt, uint4* ra, uint4* rb) const {
+  __device__ __forceinline__ void load_slice(int kt, u32x4* ra, u32x4* rb) const {
     const size_t off = (size_t)kt * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i)
-      ra[i] = pa[i] ? *reinterpret_cast<const uint4*>(pa[i] + off) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + off);
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i)
-      rb[i] = pb[i] ? *reinterpret_cast<const uint4*>(pb[i] + off) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + off);
   }
 
-  __device__ __forceinline__ static void store_slice(char* buf, const uint4* ra, const uint4* rb) {
+  __device__ __forceinline__ static void store_slice(char* buf, const u32x4* ra, const u32x4* rb) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
-      int r = chunk_row(i);
-      if (r < BM) *reinterpret_cast<uint4*>(buf + r * kLdsRow + chunk_col(i)) = ra[i];
+      const int r = chunk_row(i);
+      if ((BM * 8) % kThreads == 0 || r < BM) *reinterpret_cast<u32x4*>(buf + lds_off(r, chunk_col(i))) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
-      int r = chunk_row(i);
-      if (r < BN) *reinterpret_cast<uint4*>(buf + (BM + r) * kLdsRow + chunk_col(i)) = rb[i];
+      const int r = chunk_row(i);
+      if ((BN * 8) % kThreads == 0 || r < BN)
+        *reinterpret_cast<u32x4*>(buf + lds_off(BM + r, chunk_col(i))) = rb[i];
+    }
+  }
+
+  // Fragment of row r for the 32-wide k-step ks: lane group grp takes elements
+  // [8 grp, 8 grp + 8) of the step (16 bytes of bf16, 32 bytes of fp32).
+  __device__ __forceinline__ static frag load_frag(const char* buf, int r, int ks, int grp) {
+    if constexpr (sizeof(T) == 2) {
+      return frag{*reinterpret_cast<const uint4*>(buf + lds_off(r, ks * 4 + grp))};
+    } else {
+      const int c0 = grp * 2;  // one k-step per slice for fp32
+      frag f;
+      f.a = *reinterpret_cast<const float4*>(buf + lds_off(r, c0));
+      f.b = *reinterpret_cast<const float4*>(buf + lds_off(r, c0 + 1));
+      return f;
     }
   }
 
@@ -101,14 +122,11 @@ struct GemmTile {
     const int r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      const int koff = ks * 32 * (int)sizeof(T) + grp * 8 * (int)sizeof(T);
       frag xa[kTM], wb[kTN];
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
-        xa[i] = MF::load(reinterpret_cast<const T*>(buf + (wm * kTM * 16 + i * 16 + r16) * kLdsRow + koff));
+      for (int i = 0; i < kTM; ++i) xa[i] = load_frag(buf, wm * kTM * 16 + i * 16 + r16, ks, grp);
 #pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        wb[j] = MF::load(reinterpret_cast<const T*>(buf + (BM + wn * kTN * 16 + j * 16 + r16) * kLdsRow + koff));
+      for (int j = 0; j < kTN; ++j) wb[j] = load_frag(buf, BM + wn * kTN * 16 + j * 16 + r16, ks, grp);
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -117,18 +135,37 @@ struct GemmTile {
   }
 
   // Full K loop over nk slices. lds: kLdsBytes of shared memory.
+  //
+  // Global loads run three slices ahead of the MFMAs: slice k+1 goes from its register
+  // stage to the idle LDS buffer right after slice k's products, and that stage is
+  // refilled at once with slice k+4. One barrier per slice. The three stages are named
+  // variables and the loop is unrolled by hand, so nothing is indexed at run time.
+  struct Stage {
+    u32x4 a[kAChunks];
+    u32x4 b[kBChunks];
+  };
+  __device__ __forceinline__ void step(char* lds, int kt, int nk, Stage& st) {
+    if (kt >= nk) return;
+    compute_slice(lds + (kt & 1) * kBufBytes);
+    if (kt + 1 < nk) {
+      store_slice(lds + ((kt + 1) & 1) * kBufBytes, st.a, st.b);
+      if (kt + 4 < nk) load_slice(kt + 4, st.a, st.b);
+    }
+    __syncthreads();
+  }
   __device__ __forceinline__ void run(char* lds, int nk) {
     zero_acc();
-    uint4 ra[kAChunks], rb[kBChunks];
-    load_slice(0, ra, rb);
-    store_slice(lds, ra, rb);
+    Stage s0, s1, s2;
+    load_slice(0, s0.a, s0.b);
+    if (nk > 1) load_slice(1, s1.a, s1.b);
+    if (nk > 2) load_slice(2, s2.a, s2.b);
+    store_slice(lds, s0.a, s0.b);
+    if (nk > 3) load_slice(3, s0.a, s0.b);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) load_slice(kt + 1, ra, rb);
-      compute_slice(lds + (kt & 1) * kBufBytes);
-      if (more) store_slice(lds + ((kt + 1) & 1) * kBufBytes, ra, rb);
-      __syncthreads();
+    for (int k0 = 0; k0 < nk; k0 += 3) {
+      step(lds, k0, nk, s1);      // slice k0+1 is in s1
+      step(lds, k0 + 1, nk, s2);  // slice k0+2 is in s2
+      step(lds, k0 + 2, nk, s0);  // slice k0+3 is in s0
     }
   }
 

@@ -16,16 +16,18 @@ template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* table, const T* shift, const T* scale, float* x0, T* tap,
                         int rows, int H, int vocab, hipStream_t s);
 
-// ---- dense GEMMs (A [M,K] rows, B [N,K] rows)
+// ---- dense GEMMs (A [M,K] rows, B [N,K] rows). part/part_bytes: fp32 scratch for the
+// split-K path taken when M <= 64 (NULL: no split).
 template <typename T>
 hipError_t launch_gemm_store(const T* A, int lda, const T* B, int ldb, int M, int N, int K, T* C, int ldc,
-                             hipStream_t s);
+                             float* part, size_t part_bytes, hipStream_t s);
 template <typename T>
 hipError_t launch_gemm_merge(const T* O, const T* Wo, int M, int H, int K, const float* x, const T* hsb, const T* hss,
-                             const T* rb, const T* rs, float* h, T* a_tap, hipStream_t s);
+                             const T* rb, const T* rs, float* h, T* a_tap, float* part, size_t part_bytes,
+                             hipStream_t s);
 template <typename T>
 hipError_t launch_gemm_router_in(const T* hn, const T* Wd, int M, int R, int H, const T* b, const T* rss,
-                                 const T* s_in, T* u, hipStream_t s);
+                                 const T* s_in, T* u, float* part, size_t part_bytes, hipStream_t s);
 
 // ---- CCA projection
 template <typename T>
@@ -64,7 +66,9 @@ struct AttnArgs {
   int B, S, nh, nkv, d, cap, window;
 };
 template <typename T>
-hipError_t launch_attn_prefill(const AttnArgs<T>& a, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnArgs<T>& a, float* part, int NC, hipStream_t s);
+int attn_prefill_chunks(int S, int max_cache_len, int window);
+size_t attn_prefill_part_bytes(int B, int S, int nkv, int G, int d, int NC);
 template <typename T>
 hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s);
 size_t attn_decode_part_bytes(int B, int nkv, int G, int d);

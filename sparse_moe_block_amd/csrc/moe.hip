@@ -112,7 +112,7 @@ __global__ __launch_bounds__(WM* WN * 64) void moe_gateup_kernel(MoeArgs<T> a) {
   const int base = a.offsets[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
-  t.set_a([&](int r) -> const T* { return r < rows ? a.hn + (size_t)a.ids[base + r] * a.H : nullptr; });
+  t.set_a([&](int r) -> const T* { return a.hn + (size_t)a.ids[base + min(r, rows - 1)] * a.H; });
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
   t.set_b([&](int r) -> const T* {
     const int blk = r >> 4, w16 = r & 15;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(WM* WN * 64) void moe_down_kernel(MoeArgs<T> a) {
   const int base = a.offsets[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
-  t.set_a([&](int r) -> const T* { return r < rows ? a.neurons + (size_t)(base + r) * a.I : nullptr; });
+  t.set_a([&](int r) -> const T* { return a.neurons + (size_t)(base + min(r, rows - 1)) * a.I; });
   const T* Wd = a.W_dn + (size_t)e * a.H * a.I;
   t.set_b([&](int r) -> const T* { return Wd + (size_t)(n0 + r) * a.I; });
   t.run(smem, a.I / Tile::kBK);

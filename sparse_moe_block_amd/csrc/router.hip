@@ -26,22 +26,27 @@ constexpr int kRouterR = 256;
 template <typename T>
 __device__ __forceinline__ void router_fc(const T* __restrict__ W, const T* __restrict__ bias, const T* in_s,
                                           T* out_s, int ldsrow) {
-  // out[t][n] = rnd(gelu(rnd(sum_k in[t][k] W[n][k] + b[n]))), t < 16, n < 256
+  // out[t][n] = rnd(gelu(rnd(sum_k in[t][k] W[n][k] + b[n]))), t < 16, n < 256.
+  // The wave's 64 weight rows (its whole K range) are fetched into registers before the
+  // first MFMA so the loads overlap instead of queueing behind each product.
   using MF = Mfma<T>;
+  constexpr int KS = kRouterR / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
+  typename MF::frag wf[4][KS];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      wf[nb][ks] = MF::load(W + (size_t)(wave * 64 + nb * 16 + r16) * kRouterR + ks * 32 + grp * 8);
   f32x4 acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < kRouterR / 32; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const typename MF::frag xf = MF::load(in_s + r16 * ldsrow + ks * 32 + grp * 8);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = wave * 64 + nb * 16 + r16;
-      const typename MF::frag wf = MF::load(W + (size_t)n * kRouterR + ks * 32 + grp * 8);
-      acc[nb] = MF::mma(wf, xf, acc[nb]);
-    }
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = MF::mma(wf[nb][ks], xf, acc[nb]);
   }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -65,25 +70,46 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs<T> a) {
   __shared__ __attribute__((aligned(16))) T a2_s[kRouterTok * ROW];
   __shared__ float lg_s[kRouterTok][64];
   __shared__ int cls_s[kRouterTok];
+  __shared__ double ex_s[kRouterTok][64];
+  __shared__ double mx_s[kRouterTok];
+  __shared__ __attribute__((aligned(16))) T wout_s[64 * ROW];  // out_proj rows, staged once
 
   const int tok0 = blockIdx.x * kRouterTok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.E, NC = a.E + 1;
 
-  // RMSNorm of u: wave w handles tokens 4w..4w+3, lane owns 4 consecutive values
-  for (int tt = 0; tt < 4; ++tt) {
-    const int t = wave * 4 + tt;
-    const int tok = tok0 + t;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (tok < a.ntok) load4(a.u + (size_t)tok * kRouterR + lane * 4, v);
-    float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)kRouterR + a.eps);
-    float g[4], o[4];
+  // stage out_proj (E+1 rows of R) in LDS with coalesced 16-byte loads
+  {
+    constexpr int E16 = 16 / (int)sizeof(T);
+    const int nchunk = NC * (kRouterR / E16);
+    for (int ch = threadIdx.x; ch < nchunk; ch += blockDim.x) {
+      const int r = ch / (kRouterR / E16), col = (ch % (kRouterR / E16)) * E16;
+      *reinterpret_cast<uint4*>(wout_s + r * ROW + col) =
+          *reinterpret_cast<const uint4*>(a.Wout + (size_t)r * kRouterR + col);
+    }
+  }
+  // RMSNorm of u: wave w handles tokens 4w..4w+3, lane owns 4 consecutive values; the
+  // four rows are loaded together
+  {
+    float v[4][4], g[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = tok0 + wave * 4 + tt;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[tt][c] = 0.f;
+      if (tok < a.ntok) load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
+    }
     load4(a.norm_g + lane * 4, g);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(g[c] * Act<T>::rnd(v[c] * inv));
-    store4(z_s + t * ROW + lane * 4, o);
+    for (int tt = 0; tt < 4; ++tt) {
+      float ss = v[tt][0] * v[tt][0] + v[tt][1] * v[tt][1] + v[tt][2] * v[tt][2] + v[tt][3] * v[tt][3];
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)kRouterR + a.eps);
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(g[c] * Act<T>::rnd(v[tt][c] * inv));
+      store4(z_s + (wave * 4 + tt) * ROW + lane * 4, o);
+    }
   }
   __syncthreads();
   router_fc<T>(a.W1, a.b1, z_s, a1_s, ROW);
@@ -94,7 +120,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs<T> a) {
   // out_proj: (token, class) pairs
   for (int task = threadIdx.x; task < kRouterTok * NC; task += blockDim.x) {
     const int t = task / NC, c = task % NC;
-    const T* wr = a.Wout + (size_t)c * kRouterR;
+    const T* wr = wout_s + c * ROW;
     const T* xr = a2_s + t * ROW;
     float acc = 0.f;
     for (int k = 0; k < kRouterR; k += 4) {
@@ -110,17 +136,39 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs<T> a) {
   }
   __syncthreads();
 
-  // selection, one thread per token; softmax in double, rounded to fp32
+  // selection: softmax over the fp32 logits in double, rounded to fp32 (the exponentials
+  // and quotients of all (token, class) pairs in parallel), plus the balancing biases
+  // in fp32, first argmax
   if (threadIdx.x < kRouterTok) {
-    const int t = threadIdx.x, tok = tok0 + t;
+    const int t = threadIdx.x;
     double mx = -INFINITY;
     for (int c = 0; c < NC; ++c) mx = fmax(mx, (double)lg_s[t][c]);
+    mx_s[t] = mx;
+  }
+  __syncthreads();
+  for (int task = threadIdx.x; task < kRouterTok * NC; task += blockDim.x) {
+    const int t = task / NC, c = task % NC;
+    ex_s[t][c] = exp((double)lg_s[t][c] - mx_s[t]);
+  }
+  __syncthreads();
+  if (threadIdx.x < kRouterTok) {
+    const int t = threadIdx.x;
     double sum = 0.0;
-    for (int c = 0; c < NC; ++c) sum += exp((double)lg_s[t][c] - mx);
+    for (int c = 0; c < NC; ++c) sum += ex_s[t][c];
+    mx_s[t] = sum;
+  }
+  __syncthreads();
+  for (int task = threadIdx.x; task < kRouterTok * NC; task += blockDim.x) {
+    const int t = task / NC, c = task % NC;
+    lg_s[t][c] = (float)(ex_s[t][c] / mx_s[t]);  // probabilities replace the logits
+  }
+  __syncthreads();
+  if (threadIdx.x < kRouterTok) {
+    const int t = threadIdx.x, tok = tok0 + t;
     int best = 0;
     float best_s = -INFINITY, best_p = 0.f;
     for (int c = 0; c < NC; ++c) {
-      const float p = (float)(exp((double)lg_s[t][c] - mx) / sum);
+      const float p = lg_s[t][c];
       const float sg = p + a.bal_bias[c];
       if (sg > best_s) {
         best_s = sg;

@@ -59,9 +59,17 @@ int check_config(const zaya_block_config* c) {
   return ZAYA_OK;
 }
 
+// Key-range chunks per query tile the prefill workspace has room for: what a call
+// without cached tokens needs, and at least 4 so calls after a cache can split too.
+int prefill_chunks_ws(const zaya_block_config* c, int S) {
+  const int nc = attn_prefill_chunks(S, 0, c->sliding_window);
+  return nc < 4 ? 4 : nc;
+}
+
 // Workspace layout of one block call.
 struct Plan {
   size_t cache_len, xn, P, vdp, Q, Kw, Vw, convw, prevw, O, h, hn, logits, cls, idx, wts, offsets, ids, neurons, part;
+  size_t gpart, gpart_bytes;  // split-K partials of the few-row GEMMs
   size_t total;
 };
 
@@ -98,7 +106,12 @@ Plan plan_block(const zaya_block_config* c, int B, int S, int decode) {
   p.offsets = take((size_t)(E + 1) * 4);
   p.ids = take(T * 4);
   p.neurons = take(T * c->expert_inter * A);
-  p.part = decode ? take(attn_decode_part_bytes(B, nkv, nh / nkv, d)) : take(0);
+  p.part = decode ? take(attn_decode_part_bytes(B, nkv, nh / nkv, d))
+                  : take(attn_prefill_part_bytes(B, S, nkv, nh / nkv, d, prefill_chunks_ws(c, S)));
+  // split-K partials (only calls with at most 64 rows use them): 64 x max(N) x 16 parts
+  const size_t maxn = std::max<size_t>(std::max<size_t>(QR, H), c->router_hidden);
+  p.gpart_bytes = T <= 64 ? (size_t)64 * maxn * 16 * 4 : 0;
+  p.gpart = take(p.gpart_bytes);
   p.total = o;
   return p;
 }
@@ -188,9 +201,11 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(tap_copy(tp.attention_norm_output, xn, (size_t)T_ * H * A));
   // a2: q/k/v projections (+ the delayed value of the token before this call)
   HIPCHK(mark(1));
-  HIPCHK(launch_gemm_store<T>(xn, H, W(w->W_qkv), H, T_, QR, H, P, QR, st));
+  float* gpart = p.gpart_bytes ? (float*)(ws + p.gpart) : nullptr;
+  HIPCHK(launch_gemm_store<T>(xn, H, W(w->W_qkv), H, T_, QR, H, P, QR, gpart, p.gpart_bytes, st));
   const T* Wvd = W(w->W_qkv) + (size_t)(nh * d + nkv * d + nkv * d / 2) * H;
-  if (any_cached) HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, st));
+  if (any_cached)
+    HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, gpart, p.gpart_bytes, st));
   // a3: convolution, residual, QK norm, temperature, rotary, value halves, state
   HIPCHK(mark(2));
   CcaArgs<T> ca{P, QR, vdp, W(w->conv_w), W(w->conv_b), W(w->temp), conv_state, prev_hs, xn, cl_dev, Q, Kc, Vc, cap,
@@ -203,12 +218,15 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   if (decode)
     HIPCHK(launch_attn_decode<T>(aa, (float*)(ws + p.part), max_len, st));
   else
-    HIPCHK(launch_attn_prefill<T>(aa, st));
+    HIPCHK(launch_attn_prefill<T>(aa, (float*)(ws + p.part),
+                                  std::min(attn_prefill_chunks(S, max_len - S, c->sliding_window),
+                                           prefill_chunks_ws(c, S)),
+                                  st));
   HIPCHK(tap_copy(tp.attention_premix, O, (size_t)T_ * nh * d * A));
   // a5: o_proj + attention merge
   HIPCHK(mark(4));
   HIPCHK(launch_gemm_merge<T>(O, W(w->W_o), T_, H, nh * d, x, W(w->a_hsb), W(w->a_hss), W(w->a_rb), W(w->a_rs), h,
-                              (T*)tp.attention_output, st));
+                              (T*)tp.attention_output, gpart, p.gpart_bytes, st));
   HIPCHK(tap_copy(tp.layer_mid, h, (size_t)T_ * H * 4));
   // a6: post-attention RMSNorm
   HIPCHK(mark(5));
@@ -216,7 +234,8 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(tap_copy(tp.mlp_norm_output, hn, (size_t)T_ * H * A));
   // a7: router down_proj + carried state
   HIPCHK(mark(6));
-  HIPCHK(launch_gemm_router_in<T>(hn, W(w->r_Wd), T_, R, H, W(w->r_bd), W(w->r_rss), (const T*)s_in, (T*)s_out, st));
+  HIPCHK(launch_gemm_router_in<T>(hn, W(w->r_Wd), T_, R, H, W(w->r_bd), W(w->r_rss), (const T*)s_in, (T*)s_out, gpart,
+                                  p.gpart_bytes, st));
   // a7/a8: router MLP, selection, skip tokens' merge
   HIPCHK(mark(7));
   RouterArgs<T> ra{(const T*)s_out, W(w->r_norm_g), W(w->r_W1), W(w->r_b1), W(w->r_W2), W(w->r_b2), W(w->r_Wout),
@@ -395,12 +414,12 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
     e = launch_rmsnorm_stream<bf16_t>(xs[cur], (const bf16_t*)w->final_g, (bf16_t*)xf, T_, H, c->rms_eps, st);
     if (e == hipSuccess)
       e = launch_gemm_store<bf16_t>((const bf16_t*)xf, H, (const bf16_t*)w->embed, H, T_, cfg->vocab, H,
-                                    (bf16_t*)logits, cfg->vocab, st);
+                                    (bf16_t*)logits, cfg->vocab, nullptr, 0, st);
   } else {
     e = launch_rmsnorm_stream<float>(xs[cur], (const float*)w->final_g, (float*)xf, T_, H, c->rms_eps, st);
     if (e == hipSuccess)
       e = launch_gemm_store<float>((const float*)xf, H, (const float*)w->embed, H, T_, cfg->vocab, H,
-                                   (float*)logits, cfg->vocab, st);
+                                   (float*)logits, cfg->vocab, nullptr, 0, st);
   }
   if (e != hipSuccess) return fail(ZAYA_EHIP, "final norm / lm_head: %s", hipGetErrorString(e));
   return ZAYA_OK;

@@ -74,3 +74,24 @@ def test_all_tokens_skip():
     w["bal_bias"][cfg.num_experts] = 2.0
     run, ref, r = _full_check(cfg, w_host=w)
     assert r["routed"] == 0 and r["skipped"] == cfg.seq
+
+
+def _sample_rows(T, n=48, seed=5):
+    """Rows spread over the whole sequence: the first and last tokens, tile edges, and
+    a seeded sample in between."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 255, 256, T // 2, T - 33, T - 32, T - 2, T - 1]
+    pick = rng.choice(T, size=n, replace=False)
+    return np.unique(np.clip(np.concatenate([fixed, pick]), 0, T - 1))
+
+
+def test_full_prefill_workload_sampled_rows():
+    """The benchmark's prefill workload (batch 1, 4096 tokens, full widths) in the same
+    launch configuration: every tap on sampled rows, routing bit-exact on all tokens."""
+    cfg = CONFIGS["prefill"]
+    _full_check(cfg, rows=_sample_rows(cfg.tokens))
+
+
+def test_full_decode_workload():
+    """The benchmark's decode workload: batch 64, one new token each over 8192 cached."""
+    _full_check(CONFIGS["decode"])
