@@ -62,6 +62,25 @@ class _Hip:
 
 # ----------------------------------------------------------------------------- setup
 
+def pack_arena(tensors, dev="cuda"):
+    """Copy host tensors into one contiguous device allocation (256-byte aligned
+    sub-buffers) and return device views: a block's parameters then occupy one run of
+    pages instead of dozens of separate allocations."""
+    off, spans = 0, {}
+    for k, v in tensors.items():
+        nbytes = v.numel() * v.element_size()
+        spans[k] = (off, nbytes)
+        off += (nbytes + 255) // 256 * 256
+    arena = torch.empty(off, dtype=torch.uint8, device=dev)
+    out = {}
+    for k, v in tensors.items():
+        o, n = spans[k]
+        view = arena[o:o + n].view(v.dtype).view(v.shape)
+        view.copy_(v)
+        out[k] = view
+    return arena, out
+
+
 class Setup:
     """Device buffers of one block call (no taps)."""
 
@@ -69,7 +88,7 @@ class Setup:
         self.cfg = cfg
         dev = "cuda"
         w = block_weights(cfg)
-        self.w = {k: v.to(dev) for k, v in w.items()}
+        self.arena, self.w = pack_arena(w, dev)
         inp = block_inputs(cfg)
         B, S, H, R = cfg.batch, cfg.seq, cfg.hidden_size, cfg.router_hidden
         self.x = inp["x"].to(dev)
@@ -255,6 +274,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (a kernel of known traffic for "
+                         "scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the block's multi-GPU sharding is a design "
@@ -263,6 +285,14 @@ def main():
     hip = _Hip()
     torch.cuda.init()
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     pcfg = CONFIGS["prefill"]
     pre = measure(pcfg, args.steps, args.warmup, hip)
     print(f"[bench] prefill {pre['ms']:.4f} ms/step", file=sys.stderr, flush=True)

@@ -29,14 +29,26 @@ constexpr int kPrefillChunkTiles = 16;  // longest run of 64-key tiles one prefi
 
 // ----------------------------------------------------------------------------- prefill
 
+// LDS tiles of one 64-key block, unpadded and XOR-swizzled so that the MFMA fragment
+// reads (16 rows, one column block) and the tile writes (the transposing V write
+// included) each touch distinct banks:
+//   K   [64 keys][D]: 16-byte chunk c of key row k stored at chunk c ^ (k % chunks/row);
+//   V^T [D][64 keys]: 4-key unit u of dim row d stored at unit u ^ vswz(d).
 template <typename T, int D>
 struct AttnLds {
   static constexpr int kKeys = 64;
-  static constexpr int kKRow = D * (int)sizeof(T) + 16;   // K tile row stride (bytes)
-  static constexpr int kVRow = kKeys * (int)sizeof(T) + 16;  // V^T tile row stride (bytes)
+  static constexpr int kKRow = D * (int)sizeof(T);          // bytes per K row
+  static constexpr int kKChunksRow = kKRow / 16;
+  static constexpr int kVRow = kKeys * (int)sizeof(T);      // bytes per V^T row
+  static constexpr int kVUnit = 4 * (int)sizeof(T);         // bytes of a 4-key unit
   static constexpr int kKBytes = kKeys * kKRow;
   static constexpr int kVBytes = D * kVRow;
   static constexpr int kBytes = kKBytes + kVBytes;
+  __device__ __forceinline__ static int koff(int key, int chunk) {
+    return key * kKRow + ((chunk ^ (key & (kKChunksRow - 1))) << 4);
+  }
+  __device__ __forceinline__ static int vswz(int d) { return ((d >> 3) & 15) ^ ((d & 7) << 1); }
+  __device__ __forceinline__ static int voff(int d, int unit) { return d * kVRow + (unit ^ vswz(d)) * kVUnit; }
 };
 
 // Global -> registers for one 64-key tile: K rows as 16-byte chunks, V as 4-key x 8-dim
@@ -92,8 +104,8 @@ __device__ __forceinline__ void attn_store_tile(char* lds, const uint4* kr, cons
   for (int i = 0; i < KC; ++i) {
     const int c = threadIdx.x + i * NT;
     if (c < TR::kKChunks) {
-      const int key = c / per_row, colb = (c % per_row) * 16;
-      *reinterpret_cast<uint4*>(lds + key * L::kKRow + colb) = kr[i];
+      const int key = c / per_row, chunk = c % per_row;
+      *reinterpret_cast<uint4*>(lds + L::koff(key, chunk)) = kr[i];
     }
   }
   char* vt = lds + L::kKBytes;
@@ -108,11 +120,11 @@ __device__ __forceinline__ void attn_store_tile(char* lds, const uint4* kr, cons
     for (int kk = 0; kk < 4; ++kk) e[kk] = reinterpret_cast<const T*>(&vr[(i * 4 + kk) * VW]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      T* dst = reinterpret_cast<T*>(vt + (db8 * 8 + j) * L::kVRow) + 4 * q4;
+      T* dst = reinterpret_cast<T*>(vt + L::voff(db8 * 8 + j, q4));
       if constexpr (sizeof(T) == 2) {
         uint2 w;
         w.x = (uint32_t)e[0][j] | ((uint32_t)e[1][j] << 16);
-        w.y = (uint32_t)e[2][j] | ((uint32_t)e[3][j] << 16);
+        w.y = (uint32_t)e[2][j] | ((uint32_t)e[3][j] << 16);  // keys 4 q4 .. 4 q4 + 3
         *reinterpret_cast<uint2*>(dst) = w;
       } else {
         *reinterpret_cast<float4*>(dst) = make_float4(e[0][j], e[1][j], e[2][j], e[3][j]);
@@ -121,18 +133,35 @@ __device__ __forceinline__ void attn_store_tile(char* lds, const uint4* kr, cons
   }
 }
 
+// V^T fragment for dim row drow and the 32-key block c: keys 32c + 4 grp .. +3 then
+// 32c + 16 + 4 grp .. +3 (the order the score registers hold them in).
 template <typename T, int D>
 __device__ __forceinline__ typename Mfma<T>::frag load_vt_frag(const char* vt, int drow, int c, int grp) {
   using L = AttnLds<T, D>;
-  const T* row = reinterpret_cast<const T*>(vt + drow * L::kVRow);
   typename Mfma<T>::frag f;
   if constexpr (sizeof(T) == 2) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * c + 4 * grp);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * c + 16 + 4 * grp);
+    const uint2 lo = *reinterpret_cast<const uint2*>(vt + L::voff(drow, 8 * c + grp));
+    const uint2 hi = *reinterpret_cast<const uint2*>(vt + L::voff(drow, 8 * c + 4 + grp));
     f.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
   } else {
-    f.a = *reinterpret_cast<const float4*>(row + 32 * c + 4 * grp);
-    f.b = *reinterpret_cast<const float4*>(row + 32 * c + 16 + 4 * grp);
+    f.a = *reinterpret_cast<const float4*>(vt + L::voff(drow, 8 * c + grp));
+    f.b = *reinterpret_cast<const float4*>(vt + L::voff(drow, 8 * c + 4 + grp));
+  }
+  return f;
+}
+
+// K fragment of key row `key`, d elements [32 dc + 8 grp, +8).
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::frag attn_k_frag(const char* kbuf, int key, int dc, int grp) {
+  using L = AttnLds<T, D>;
+  constexpr int CPF = 8 * (int)sizeof(T) / 16;  // 16-byte chunks per fragment (1 or 2)
+  const int c0 = (dc * 32 + grp * 8) * (int)sizeof(T) / 16;
+  typename Mfma<T>::frag f;
+  if constexpr (CPF == 1) {
+    f.v = *reinterpret_cast<const uint4*>(kbuf + L::koff(key, c0));
+  } else {
+    f.a = *reinterpret_cast<const float4*>(kbuf + L::koff(key, c0));
+    f.b = *reinterpret_cast<const float4*>(kbuf + L::koff(key, c0 + 1));
   }
   return f;
 }
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const frag kf = MF::load(reinterpret_cast<const T*>(kbuf + (kb * 16 + r16) * L::kKRow) + dc * 32 + grp * 8);
+        const frag kf = attn_k_frag<T, D>(kbuf, kb * 16 + r16, dc, grp);
         s[0][kb] = MF::mma(kf, qf[0][dc], s[0][kb]);
         s[1][kb] = MF::mma(kf, qf[1][dc], s[1][kb]);
       }
@@ -246,38 +275,46 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int qb = 0; qb < 2; ++qb) {
       const int qp = L0 + q0 + qb * 16 + r16;
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[qb][kb][i] * sscale;
-          if (!full) {
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             const int kp = k0 + kb * 16 + 4 * grp + i;
-            if (kp > qp || (W >= 0 && qp - kp > W)) v = -INFINITY;
+            if (kp > qp || (W >= 0 && qp - kp > W)) s[qb][kb][i] = -INFINITY;
+            mx = fmaxf(mx, s[qb][kb][i]);
           }
-          s[qb][kb][i] = v;
-          mx = fmaxf(mx, v);
-        }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // running maxima are kept on raw scores; the 1/sqrt(d) * log2(e) factor is folded
+      // into the exponent: p = 2^(s c - m c)
       const float m_new = fmaxf(m_run[qb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
+      const float mc = m_new == -INFINITY ? 0.f : m_new * sscale;
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(s[qb][kb][i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][i], sscale, -mc));
           s[qb][kb][i] = pv;
           ps += pv;
         }
-      l_run[qb] = l_run[qb] * alpha + ps;
+      if (__ballot(m_new != m_run[qb])) {  // some row's maximum moved: rescale
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] * sscale - mc);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
+      }
+      l_run[qb] += ps;
       m_run[qb] = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
     }
 
     // O^T += V^T P^T over two 32-key chunks
@@ -329,8 +366,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
         float v[4] = {o[qb][db][0], o[qb][db][1], o[qb][db][2], o[qb][db][3]};
         store4(pr + db * 16 + 4 * grp, v);
       }
-      if (grp == 0) {
-        pr[D] = m_run[qb];
+      if (grp == 0) {  // the combine pass works in the exponent's units: m * scale
+        pr[D] = m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * sscale;
         pr[D + 1] = l;
       }
     }

@@ -13,83 +13,140 @@
 // Q goes to [T, nh, d]; K and V to the cache at position p; conv_state and prev_hs
 // are advanced for the next call.
 //
-// Work split: one workgroup per (16-token tile, KV group, sequence); each wave takes
-// one token at a time (two when d = 64). Lane p owns the dim pair (da, db) of every
-// head of the group: for p < rope_dim/2 that pair is the rotary pair, so the rotation
-// never leaves the lane; the head norms are reductions over the d/2 lanes of a token.
+// Work split: one workgroup per (16-token tile, KV group, sequence). The tile's
+// projection rows (plus two tokens of history), the group's conv taps and biases are
+// first staged in LDS with coalesced 16-byte loads; then each wave takes one token at a
+// time (two when d = 64). Lane p owns the dim pair (da, db) of every head of the group:
+// for p < rope_dim/2 that pair is the rotary pair, so the rotation never leaves the
+// lane; the head norms are reductions over the d/2 lanes of a token.
 #include "common.h"
 #include "kernels.h"
 
 namespace zaya {
 
 constexpr int kCcaTokens = 16;
+constexpr int kCcaRows = kCcaTokens + 2;  // the tile plus two tokens of history
 
+// LDS layout of one tile (act elements, row r = token t0 - 2 + r):
+//   xs[r][0 .. G*d)        q channels of the group's heads
+//   xs[r][G*d .. (G+1)*d)  k channels of the group's key head
+//   xs[r][(G+1)*d .. +d/2) v_current half of the group
+//   xs[r][.. +d/2)          v_delayed half of the group
 template <typename T>
 __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
+  extern __shared__ __attribute__((aligned(16))) char cca_lds[];
   const int b = blockIdx.z, g = blockIdx.y, tile = blockIdx.x;
   const int d = a.d, nh = a.nh, nkv = a.nkv, G = nh / nkv, r = a.rope_dim;
-  const int spt = d / 2;          // lanes per token
-  const int tpw = 64 / spt;       // tokens per wave step
+  const int GC = (G + 1) * d;          // q and k channels of the group
+  const int ROWE = GC + d;             // + both value halves
+  T* xs = reinterpret_cast<T*>(cca_lds);
+  float* wsm = reinterpret_cast<float*>(cca_lds + ((kCcaRows * ROWE * (int)sizeof(T) + 15) & ~15));
+  // wsm[c*4 + 0..2] = conv taps of group channel c, wsm[c*4 + 3] = its bias
+  const int S = a.S, QR = a.qkv_ld;
+  const int kcol = nh * d, vccol = nh * d + nkv * d, vdcol = vccol + nkv * d / 2;
+  const int L0 = a.cache_len[b];
+  const bool fresh = L0 == 0;
+  const int t0 = tile * kCcaTokens;
+  const int t_end = min(S, t0 + kCcaTokens);
+
+  // group channel c -> global channel (column of P, row of conv_w / conv_state)
+  auto gchan = [&](int c) { return c < G * d ? g * G * d + c : kcol + g * d + (c - G * d); };
+
+  // 1. stage projection rows of tokens t0-2 .. t_end-1 (16-byte chunks of the four
+  //    contiguous segments), and the history rows from conv_state / zeros
+  {
+    constexpr int E16 = 16 / (int)sizeof(T);
+    const int segq = G * d / E16, segk = d / E16, segv = (d / 2) / E16;
+    const int per_row = segq + segk + 2 * segv;
+    const int nrows = t_end - t0 + 2;
+    for (int ch = threadIdx.x; ch < nrows * per_row; ch += blockDim.x) {
+      const int rr = ch / per_row, cc = ch % per_row;
+      const int t = t0 - 2 + rr;
+      int src, dst;
+      if (cc < segq) {
+        src = g * G * d + cc * E16;
+        dst = cc * E16;
+      } else if (cc < segq + segk) {
+        src = kcol + g * d + (cc - segq) * E16;
+        dst = G * d + (cc - segq) * E16;
+      } else if (cc < segq + segk + segv) {
+        src = vccol + g * (d / 2) + (cc - segq - segk) * E16;
+        dst = GC + (cc - segq - segk) * E16;
+      } else {
+        src = vdcol + g * (d / 2) + (cc - segq - segk - segv) * E16;
+        dst = GC + d / 2 + (cc - segq - segk - segv) * E16;
+      }
+      if (t >= 0)  // rows before the sequence start are the history, filled below
+        *reinterpret_cast<uint4*>(xs + rr * ROWE + dst) =
+            *reinterpret_cast<const uint4*>(a.P + ((size_t)b * S + t) * QR + src);
+    }
+    // history (tokens -2, -1 of a sequence with cached tokens): q/k channels from
+    // conv_state, the delayed value from prev_hs @ W_vd^T
+    if (t0 == 0) {
+      for (int i = threadIdx.x; i < 2 * GC; i += blockDim.x) {
+        const int rr = i / GC, c = i % GC;
+        const T v = fresh ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + rr];
+        xs[rr * ROWE + c] = v;
+      }
+      for (int i = threadIdx.x; i < d / 2; i += blockDim.x)
+        xs[1 * ROWE + GC + d / 2 + i] =
+            fresh ? Act<T>::cvt(0.f) : a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + i];
+    }
+    for (int c = threadIdx.x; c < GC; c += blockDim.x) {
+      const int gc = gchan(c);
+      wsm[c * 4 + 0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
+      wsm[c * 4 + 1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
+      wsm[c * 4 + 2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
+      wsm[c * 4 + 3] = Act<T>::tof(a.conv_b[gc]);
+    }
+  }
+  __syncthreads();
+
+  // 2. compute: lane p owns the dim pair (da, db) of every head of the group
+  const int spt = d / 2;     // lanes per token
+  const int tpw = 64 / spt;  // tokens per wave step
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / spt, p = lane % spt;
   const int da = p < r / 2 ? p : r + (p - r / 2);
   const int db = p < r / 2 ? p + r / 2 : r + (d - r) / 2 + (p - r / 2);
-  const int L0 = a.cache_len[b];
-  const bool fresh = L0 == 0;
-  const int S = a.S, QR = a.qkv_ld;
-  const int kcol = nh * d, vccol = nh * d + nkv * d, vdcol = vccol + nkv * d / 2;
   const float sqrt_d = sqrtf((float)d);
   const float temp = Act<T>::tof(a.temp[g]);
-  // rotary inverse frequency of this lane's pair, in double for large positions
   const double inv_freq = p < r / 2 ? pow((double)a.theta, -2.0 * (double)p / (double)r) : 0.0;
-
-  const int t_begin = tile * kCcaTokens;
-  const int t_end = min(S, t_begin + kCcaTokens);
-  for (int base = t_begin + wave * tpw; base < t_end; base += 4 * tpw) {
+  for (int base = t0 + wave * tpw; base < t_end; base += 4 * tpw) {
     const int t = base + sub;
     const bool active = t < t_end;
-    const int tt = active ? t : t_end - 1;  // inactive half-waves mirror a valid token; results discarded
-    const size_t row = (size_t)b * S + tt;
-    // gather x(t-2), x(t-1), x(t) for channel c (q or k) at dims da, db
-    auto xval = [&](int c, int dt) -> float {
-      const int ts = tt - dt;
-      if (ts >= 0) return Act<T>::tof(a.P[((size_t)b * S + ts) * QR + c]);
-      if (fresh) return 0.f;
-      return Act<T>::tof(a.conv_state[((size_t)b * a.C + c) * 2 + (2 + ts)]);  // ts = -2 -> slot 0, -1 -> slot 1
-    };
+    const int tt = active ? t : t_end - 1;
+    const int rr = tt - t0 + 2;  // LDS row of token tt
+    const T* x0 = xs + rr * ROWE;  // t
+    const T* x1 = x0 - ROWE;       // t - 1
+    const T* x2 = x1 - ROWE;       // t - 2
     auto conv = [&](int c) -> float {
-      const float w0 = Act<T>::tof(a.conv_w[c * 3 + 0]), w1 = Act<T>::tof(a.conv_w[c * 3 + 1]);
-      const float w2 = Act<T>::tof(a.conv_w[c * 3 + 2]);
-      return Act<T>::tof(a.conv_b[c]) + w0 * xval(c, 2) + w1 * xval(c, 1) + w2 * xval(c, 0);
+      const float* w = wsm + c * 4;
+      return w[3] + w[0] * Act<T>::tof(x2[c]) + w[1] * Act<T>::tof(x1[c]) + w[2] * Act<T>::tof(x0[c]);
     };
-    // key head
-    const int kca = kcol + g * d + da, kcb = kcol + g * d + db;
-    const float pka = Act<T>::tof(a.P[row * QR + kca]), pkb = Act<T>::tof(a.P[row * QR + kcb]);
+    const int kca = G * d + da, kcb = G * d + db;
+    const float pka = Act<T>::tof(x0[kca]), pkb = Act<T>::tof(x0[kcb]);
     float qa[8], qb[8];
     float rka = 0.f, rkb = 0.f;
     for (int hh = 0; hh < G; ++hh) {
-      const int h = g * G + hh;
-      const int ca = h * d + da, cb = h * d + db;
-      const float pqa = Act<T>::tof(a.P[row * QR + ca]), pqb = Act<T>::tof(a.P[row * QR + cb]);
-      const float rqa = (pqa + pka) * 0.5f, rqb = (pqb + pkb) * 0.5f;
+      const int ca = hh * d + da, cb = hh * d + db;
+      const float rqa = (Act<T>::tof(x0[ca]) + pka) * 0.5f, rqb = (Act<T>::tof(x0[cb]) + pkb) * 0.5f;
       rka += rqa;
       rkb += rqb;
       qa[hh] = conv(ca) + rqa;
       qb[hh] = conv(cb) + rqb;
     }
-    float ka = conv(kca) + rka / (float)G;
-    float kb = conv(kcb) + rkb / (float)G;
-    // rotary angle for position L0 + t
+    const float ka = conv(kca) + rka / (float)G;
+    const float kb = conv(kcb) + rkb / (float)G;
     float cs = 1.f, sn = 0.f;
     if (p < r / 2) {
-      double ang = (double)(L0 + tt) * inv_freq;
       double sd, cd;
-      sincos(ang, &sd, &cd);
+      sincos((double)(L0 + tt) * inv_freq, &sd, &cd);
       cs = (float)cd;
       sn = (float)sd;
     }
+    const size_t row = (size_t)b * S + tt;
     const size_t pos = (size_t)(L0 + tt);
-    // queries
     for (int hh = 0; hh < G; ++hh) {
       const int h = g * G + hh;
       const float ss = group_sum(qa[hh] * qa[hh] + qb[hh] * qb[hh], spt);
@@ -120,22 +177,16 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         va = ra;
         vb = rb;
       }
-      // values: current half of token t, delayed half of token t-1
-      auto vval = [&](int x) -> float {
-        if (x < d / 2) return Act<T>::tof(a.P[row * QR + vccol + g * (d / 2) + x]);
-        const int xx = x - d / 2;
-        if (tt > 0) return Act<T>::tof(a.P[(row - 1) * QR + vdcol + g * (d / 2) + xx]);
-        if (fresh) return 0.f;
-        return Act<T>::tof(a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + xx]);
-      };
-      const float vda = vval(da), vdb = vval(db);
+      // values: current half of token t, delayed half of token t - 1
+      auto vval = [&](int x) -> T { return x < d / 2 ? x0[GC + x] : x1[GC + x]; };
+      const T vda = vval(da), vdb = vval(db);
       if (active) {
         T* ko = a.K + (((size_t)b * nkv + g) * a.cap + pos) * d;
         T* vo = a.V + (((size_t)b * nkv + g) * a.cap + pos) * d;
         ko[da] = Act<T>::cvt(va);
         ko[db] = Act<T>::cvt(vb);
-        vo[da] = Act<T>::cvt(vda);
-        vo[db] = Act<T>::cvt(vdb);
+        vo[da] = vda;
+        vo[db] = vdb;
         if (a.k_tap) {
           T* kt = a.k_tap + (((size_t)b * nkv + g) * S + tt) * d;
           kt[da] = Act<T>::cvt(va);
@@ -143,40 +194,45 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         }
         if (a.v_tap) {
           T* vt = a.v_tap + (((size_t)b * nkv + g) * S + tt) * d;
-          vt[da] = Act<T>::cvt(vda);
-          vt[db] = Act<T>::cvt(vdb);
+          vt[da] = vda;
+          vt[db] = vdb;
         }
       }
     }
   }
 
-  // State for the next call. Only the first tile of a sequence reads the old conv
-  // state (tokens 0 and 1), so that tile rewrites it after everyone in it is done.
+  // 3. state for the next call. Only tile 0 reads the old conv_state (in step 1, before
+  //    the barrier above), so tile 0 also writes the new one: the q/k conv inputs of
+  //    tokens S-2 and S-1 (from P; for S == 1 the older slot is the old slot 1, which
+  //    this tile holds in LDS). The last token's normed input becomes prev_hs.
   if (tile == 0) {
-    __syncthreads();
-    const int nch = (G + 1) * d;
-    for (int i = threadIdx.x; i < nch; i += blockDim.x) {
-      const int c = i < G * d ? g * G * d + i : kcol + g * d + (i - G * d);
-      T* cs = a.conv_state + ((size_t)b * a.C + c) * 2;
-      const T zero = Act<T>::cvt(0.f);
-      const T old1 = fresh ? zero : cs[1];
-      const T s0 = S >= 2 ? a.P[((size_t)b * S + S - 2) * QR + c] : old1;
-      const T s1 = a.P[((size_t)b * S + S - 1) * QR + c];
+    for (int c = threadIdx.x; c < GC; c += blockDim.x) {
+      const int gc = gchan(c);
+      T* cs = a.conv_state + ((size_t)b * a.C + gc) * 2;
+      const T s0 = S >= 2 ? a.P[((size_t)b * S + S - 2) * QR + gc] : xs[1 * ROWE + c];
+      const T s1 = a.P[((size_t)b * S + S - 1) * QR + gc];
       cs[0] = s0;
       cs[1] = s1;
     }
   }
-  if (tile == gridDim.x - 1 && g == 0) {
+  if (t_end == S && g == 0) {
     const T* src = a.xn + ((size_t)b * S + S - 1) * a.H;
     T* dst = a.prev_hs + (size_t)b * a.H;
     for (int i = threadIdx.x; i < a.H; i += blockDim.x) dst[i] = src[i];
   }
 }
 
+size_t cca_lds_bytes(int d, int G, int act_bytes) {
+  const int GC = (G + 1) * d;
+  const size_t xs = ((size_t)kCcaRows * (GC + d) * act_bytes + 15) & ~(size_t)15;
+  return xs + (size_t)GC * 4 * sizeof(float);
+}
+
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s) {
   dim3 grid((a.S + kCcaTokens - 1) / kCcaTokens, a.nkv, a.B);
-  hipLaunchKernelGGL(cca_kernel<T>, grid, dim3(256), 0, s, a);
+  const size_t lds = cca_lds_bytes(a.d, a.nh / a.nkv, (int)sizeof(T));
+  hipLaunchKernelGGL(cca_kernel<T>, grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

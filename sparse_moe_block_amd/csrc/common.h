@@ -72,6 +72,13 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Two floats -> packed bf16 pair (low half = lo), hardware round-to-nearest-even.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // MFMA fragment traits.
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -83,13 +90,13 @@ template <> struct Mfma<bf16_t> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v), __builtin_bit_cast(bf16x8_t, b.v),
                                                    c, 0, 0, 0);
   }
-  // Build a fragment from 8 floats (rounding each to bf16).
+  // Build a fragment from 8 floats (each rounded to the nearest bf16).
   __device__ __forceinline__ static frag pack(const float* f) {
     frag r;
-    r.v.x = (uint32_t)f2bf(f[0]) | ((uint32_t)f2bf(f[1]) << 16);
-    r.v.y = (uint32_t)f2bf(f[2]) | ((uint32_t)f2bf(f[3]) << 16);
-    r.v.z = (uint32_t)f2bf(f[4]) | ((uint32_t)f2bf(f[5]) << 16);
-    r.v.w = (uint32_t)f2bf(f[6]) | ((uint32_t)f2bf(f[7]) << 16);
+    r.v.x = pack_bf16x2(f[0], f[1]);
+    r.v.y = pack_bf16x2(f[2], f[3]);
+    r.v.z = pack_bf16x2(f[4], f[5]);
+    r.v.w = pack_bf16x2(f[6], f[7]);
     return r;
   }
 };
