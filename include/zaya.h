@@ -145,7 +145,7 @@ typedef struct zaya_cca_cache {
  *   expert_classes [B,S] int32 (E = skip); expert_indices [B,S] int32;
  *   expert_weights [B,S] act; bucket_offsets [E+1] int32; bucket_ids [T] int32 (first
  *   bucket_offsets[E] used); mlp_neurons [T, I] act in bucket order; routed_output,
- *   mlp_output [B,S,H] act. */
+ *   mlp_output [B,S,H] act; layer_output [B,S,H] fp32; router_state [B,S,R] act. */
 typedef struct zaya_taps {
   void* attention_norm_output;
   void* attention_queries;
@@ -164,6 +164,8 @@ typedef struct zaya_taps {
   void* mlp_neurons;
   void* routed_output;
   void* mlp_output;
+  float* layer_output;  /* [B,S,H] fp32: the stream leaving the block (same as x_out) */
+  void* router_state;   /* [B,S,R] act: the router state handed to the next block */
 } zaya_taps;
 
 /* Workspace (device bytes) needed by one block call of B sequences of S tokens

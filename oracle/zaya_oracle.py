@@ -515,7 +515,7 @@ def embed(cfg, sw, ids):
     reading: shift and scale are [H] vectors applied in that order.)
     """
     rnd = rounder(cfg.act_dtype)
-    e = f64(sw["embed"])[np.asarray(ids)]
+    e = f64(np.asarray(sw["embed"])[np.asarray(ids)])
     te = rnd(rnd(e + f64(sw["emb_shift"])) * f64(sw["emb_scale"]))
     return te, rnd_f32(te)
 

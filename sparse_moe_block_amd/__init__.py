@@ -55,7 +55,8 @@ class CcaCache(C.Structure):
 
 TAP_FIELDS = ("attention_norm_output", "attention_queries", "attention_keys", "attention_values", "attention_premix",
               "attention_output", "layer_mid", "mlp_norm_output", "router_logits", "expert_classes", "expert_indices",
-              "expert_weights", "bucket_offsets", "bucket_ids", "mlp_neurons", "routed_output", "mlp_output")
+              "expert_weights", "bucket_offsets", "bucket_ids", "mlp_neurons", "routed_output", "mlp_output",
+              "layer_output", "router_state")
 
 
 class Taps(C.Structure):

@@ -260,6 +260,8 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(launch_moe_down<T>(ma, st));
   HIPCHK(mark(11));
   HIPCHK(tap_copy(tp.mlp_neurons, neurons, (size_t)T_ * I * A));
+  HIPCHK(tap_copy(tp.layer_output, x_out, (size_t)T_ * H * 4));
+  HIPCHK(tap_copy(tp.router_state, s_out, (size_t)T_ * R * A));
   return ZAYA_OK;
 }
 

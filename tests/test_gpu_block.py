@@ -95,3 +95,23 @@ def test_full_prefill_workload_sampled_rows():
 def test_full_decode_workload():
     """The benchmark's decode workload: batch 64, one new token each over 8192 cached."""
     _full_check(CONFIGS["decode"])
+
+
+def test_long_context_window_zipf_sampled_rows():
+    """The long-context workload: 32768 tokens, sliding window 4096 (4097 keys), and
+    balancing biases calibrated by the oracle (tests/golden/make_longctx_bias.py) so the
+    expert load follows Zipf(1.2) with 15% skip. Sampled rows include the window edge."""
+    import os
+    from zaya_synth import block_weights
+    cfg = CONFIGS["longctx"]
+    path = os.path.join(os.path.dirname(__file__), "golden", "longctx_bal_bias.txt")
+    bb = np.array([float(l) for l in open(path) if l.strip() and not l.startswith("#")])
+    w = block_weights(cfg, bal_bias=bb)
+    T = cfg.tokens
+    rows = np.unique(np.concatenate([_sample_rows(T, n=40), [4095, 4096, 4097, 4098, 8191, 8192, 16384]]))
+    run, ref, r = _full_check(cfg, rows=rows, w_host=w)
+    offs = run.taps["bucket_offsets"].cpu().numpy()
+    counts = np.diff(offs)
+    print("long context expert counts:", counts.tolist(), "skip:", T - int(offs[-1]), flush=True)
+    # the load is strongly skewed: the first expert carries several times the last one's tokens
+    assert counts[0] > 5 * counts[-1] and (T - offs[-1]) > 0.1 * T

@@ -232,6 +232,62 @@ def block_weights(cfg: ZayaConfig, block: int = 0, seed: int = 0,
     return w
 
 
+def _device_stream(seed: int, cfg_name: str, block: int, tensor: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    key = (int(seed) * 1000003 + zlib.crc32(cfg_name.encode()) * 8191 + (int(block) + 1) * 131
+           + zlib.crc32(tensor.encode())) % (2 ** 63)
+    g.manual_seed(key)
+    return g
+
+
+def block_weights_device(cfg: ZayaConfig, block: int = 0, seed: int = 0, device="cuda") -> Dict[str, torch.Tensor]:
+    """The same recipe as ``block_weights`` drawn directly on the device (torch's own
+    counter-based generator, one stream per tensor): for large stacks, where drawing
+    40 blocks on the host takes minutes. Values differ from ``block_weights``; every
+    consumer of a run reads the same tensors."""
+    shapes = block_weight_shapes(cfg)
+    dt = cfg.torch_dtype
+    n = cfg.name
+
+    def N(t, mean=0.0, std=0.02):
+        x = torch.randn(shapes[t], generator=_device_stream(seed, n, block, t, device), device=device,
+                        dtype=torch.float32)
+        return (x * std + mean).to(dt)
+
+    def gain(t):
+        return torch.ones(shapes[t], device=device, dtype=dt) if cfg.gain_std == 0.0 else N(t, 1.0, cfg.gain_std)
+
+    lo, hi = cfg.temp_range
+    tg = _device_stream(seed, n, block, "temp", device)
+    temp = torch.rand(shapes["temp"], generator=tg, device=device) * (hi - lo) + lo
+    w = {
+        "ln1_g": gain("ln1_g"), "W_qkv": N("W_qkv"), "conv_w": N("conv_w", std=cfg.conv_std),
+        "conv_b": N("conv_b", std=cfg.conv_std), "temp": temp.to(dt), "W_o": N("W_o"),
+        "a_hsb": N("a_hsb", std=0.01), "a_hss": N("a_hss", 1.0, 0.05), "a_rb": N("a_rb", std=0.01),
+        "a_rs": N("a_rs", 1.0, 0.05), "ln2_g": gain("ln2_g"),
+        "r_Wd": N("r_Wd"), "r_bd": N("r_bd"), "r_rss": N("r_rss", 1.0, 0.05), "r_norm_g": gain("r_norm_g"),
+        "r_W1": N("r_W1"), "r_b1": N("r_b1"), "r_W2": N("r_W2"), "r_b2": N("r_b2"), "r_Wout": N("r_Wout"),
+        "W_gu": N("W_gu"), "W_dn": N("W_dn"),
+        "m_hsb": N("m_hsb", std=0.01), "m_hss": N("m_hss", 1.0, 0.05), "m_rb": N("m_rb", std=0.01),
+        "m_rs": N("m_rs", 1.0, 0.05),
+        "bal_bias": torch.zeros(shapes["bal_bias"], device=device, dtype=torch.float32),
+    }
+    return w
+
+
+def stack_weights_device(cfg: ZayaConfig, seed: int = 0, device="cuda") -> Dict[str, torch.Tensor]:
+    """Embedding, shift/scale and final norm gain drawn on the device (see
+    ``block_weights_device``)."""
+    H, V, n, dt = cfg.hidden_size, cfg.vocab_size, cfg.name, cfg.torch_dtype
+
+    def N(t, shape, mean, std):
+        x = torch.randn(shape, generator=_device_stream(seed, n, -1, t, device), device=device, dtype=torch.float32)
+        return (x * std + mean).to(dt)
+
+    return {"embed": N("embed", (V, H), 0.0, 0.02), "emb_shift": N("emb_shift", (H,), 0.0, 0.01),
+            "emb_scale": N("emb_scale", (H,), 1.0, 0.05), "final_g": torch.ones(H, device=device, dtype=dt)}
+
+
 def stack_weights(cfg: ZayaConfig, seed: int = 0) -> Dict[str, torch.Tensor]:
     """Embedding (tied with lm_head), its shift/scale, and the final norm gain."""
     H, V, n = cfg.hidden_size, cfg.vocab_size, cfg.name
