@@ -165,6 +165,44 @@ def stage_work(cfg, n_routed: int, n_used: int):
     return out
 
 
+# Source files each stage's kernels are built from (for matching recorded counters).
+STAGE_SOURCES = {
+    "expert_gate_up": ["moe.hip", "gemm_core.h", "common.h", "kernels.h"],
+    "expert_down_merge": ["moe.hip", "gemm_core.h", "common.h", "kernels.h"],
+    "attention": ["attn.hip", "common.h", "kernels.h"],
+    "qkv_proj": ["gemm.hip", "gemm_core.h", "common.h", "kernels.h"],
+    "o_proj_merge": ["gemm.hip", "gemm_core.h", "common.h", "kernels.h"],
+}
+
+
+def sources_sha256(stage):
+    import hashlib
+    h = hashlib.sha256()
+    for f in STAGE_SOURCES.get(stage, []):
+        with open(os.path.join(ROOT, "sparse_moe_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(stage, workload):
+    """HBM bytes per launch of `stage` measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE
+    passes scaled by a plain-copy calibration), read from the summaries under profiles/.
+    None if no summary matches the current kernel sources."""
+    import glob
+    if stage not in STAGE_SOURCES:
+        return None
+    want = sources_sha256(stage)
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md")):
+        rec = {}
+        for line in open(path):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                rec[k.strip()] = v.strip().strip("`")
+        if rec.get("stage") == stage and rec.get("workload") == workload and rec.get("sources_sha256") == want:
+            return int(float(rec["hbm_bytes_per_launch"]))
+    return None
+
+
 def roofline(flops, nbytes, ms):
     """Bound by whichever roof the kernel's own work hits first; achieved rate on it."""
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
@@ -235,7 +273,7 @@ def measure(cfg, steps, warmup, hip):
     f, b = work[dom]
     roof = roofline(f, b, stages[dom])
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(dom, cfg.name)
     total_f = sum(v[0] for v in work.values())
     total_b = sum(v[1] for v in work.values())
     del setup
