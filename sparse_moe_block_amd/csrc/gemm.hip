@@ -70,7 +70,8 @@ struct EpiRouterIn {
 };
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void gemm_nt_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
                                                                int ldb, int M, int N, int K, Epi epi) {
   using Tile = GemmTile<T, BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
@@ -98,7 +99,7 @@ static hipError_t launch_cfg(const T* A, int lda, const T* B, int ldb, int M, in
 // 64 x 64 output tile into fp32 partials; a second pass sums the ranges in a fixed
 // order and applies the epilogue, so results do not depend on scheduling.
 template <typename T>
-__global__ __launch_bounds__(256) void gemm_splitk_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_splitk_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
                                                           int ldb, int M, int N, int K, int kparts,
                                                           float* __restrict__ part) {
   using Tile = GemmTile<T, 64, 64, 2, 2>;

@@ -34,6 +34,10 @@ struct GemmTile {
   static constexpr int kBChunks = (BN * 8 + kThreads - 1) / kThreads;
   static constexpr int kBufBytes = (BM + BN) * kRowBytes;
   static constexpr int kLdsBytes = 2 * kBufBytes;
+  // Waves per SIMD the kernel is compiled for (register budget 512 / waves): 2 for the
+  // 128x128 tiles (64 KiB of LDS already allows only two workgroups per CU), more for
+  // the smaller ones.
+  static constexpr int kWavesPerEU = BM * BN >= 128 * 128 ? 2 : 4;
   static_assert(BM % (WM * 16) == 0 && BN % (WN * 16) == 0, "tile must split into 16x16 blocks");
   static_assert(kKSteps >= 1, "slice too short");
 
@@ -140,33 +144,38 @@ struct GemmTile {
   // stage to the idle LDS buffer right after slice k's products, and that stage is
   // refilled at once with slice k+4. One barrier per slice. The three stages are named
   // variables and the loop is unrolled by hand, so nothing is indexed at run time.
+  //
+  // The main loop has no data-dependent branches: past the end, the refill re-reads the
+  // last slice (never used) and the store fills the idle buffer. Every path then has the
+  // same loads in flight, and the compiler waits only for the oldest stage instead of
+  // draining all of them before each LDS store.
   struct Stage {
     u32x4 a[kAChunks];
     u32x4 b[kBChunks];
   };
   __device__ __forceinline__ void step(char* lds, int kt, int nk, Stage& st) {
-    if (kt >= nk) return;
     compute_slice(lds + (kt & 1) * kBufBytes);
-    if (kt + 1 < nk) {
-      store_slice(lds + ((kt + 1) & 1) * kBufBytes, st.a, st.b);
-      if (kt + 4 < nk) load_slice(kt + 4, st.a, st.b);
-    }
+    store_slice(lds + ((kt + 1) & 1) * kBufBytes, st.a, st.b);
+    load_slice(min(kt + 4, nk - 1), st.a, st.b);
     __syncthreads();
   }
   __device__ __forceinline__ void run(char* lds, int nk) {
     zero_acc();
     Stage s0, s1, s2;
     load_slice(0, s0.a, s0.b);
-    if (nk > 1) load_slice(1, s1.a, s1.b);
-    if (nk > 2) load_slice(2, s2.a, s2.b);
+    load_slice(min(1, nk - 1), s1.a, s1.b);
+    load_slice(min(2, nk - 1), s2.a, s2.b);
     store_slice(lds, s0.a, s0.b);
-    if (nk > 3) load_slice(3, s0.a, s0.b);
+    load_slice(min(3, nk - 1), s0.a, s0.b);
     __syncthreads();
-    for (int k0 = 0; k0 < nk; k0 += 3) {
+    int k0 = 0;
+    for (; k0 + 3 <= nk; k0 += 3) {
       step(lds, k0, nk, s1);      // slice k0+1 is in s1
       step(lds, k0 + 1, nk, s2);  // slice k0+2 is in s2
       step(lds, k0 + 2, nk, s0);  // slice k0+3 is in s0
     }
+    if (k0 < nk) step(lds, k0, nk, s1);
+    if (k0 + 1 < nk) step(lds, k0 + 1, nk, s2);
   }
 
   // Calls f(m_local, n_local, v[4]) for every 4-column group this lane holds;

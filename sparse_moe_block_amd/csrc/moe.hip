@@ -12,9 +12,9 @@
 //   down:    y = rnd(neurons Wd^T); routed = rnd(w * y)
 //            mlp_output = rnd(rnd(routed + hsb) * hss); out = f32(f32(h + rb) * rs) + mlp_output
 //
-// Grouped GEMMs: the grid is (n tiles) x (an upper bound on the number of row tiles
-// over all experts, ceil(T/BM) + E); each workgroup walks the E+1 offsets to find
-// its (expert, row tile) and exits if it has none, so nothing waits on the host.
+// Grouped GEMMs: the grid is an upper bound on the (expert, column tile, row tile)
+// items, (ceil(T/BM) + E) x column tiles; each workgroup walks the E+1 offsets to find
+// its item (see moe_item) and exits if it has none, so nothing waits on the host.
 // Gate and up weight rows are interleaved in 16-row blocks inside each weight tile,
 // so every lane holds a gate and an up accumulator for the same outputs and SwiGLU
 // happens in registers.
@@ -82,33 +82,52 @@ hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, 
 
 // ----------------------------------------------------------------------------- grouped GEMMs
 
-// Map a row-tile slot to (expert, first row of the tile within the expert's bucket).
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off, int E, int BM, int slot, int& e_out,
-                                          int& r0_out, int& n_out) {
-  int cum = 0;
+// Work items of a grouped GEMM are (expert, column tile, row tile), expert by expert,
+// then column tile, row tile fastest. They are dealt to the 8 XCDs in contiguous runs
+// (workgroup b runs on XCD b % 8), so at any time the workgroups of one XCD work on
+// neighbouring items of one expert: they share its token rows and, across row tiles,
+// each weight tile through that XCD's L2. Returns false for workgroups past the real
+// items (the grid is sized for the worst case on the host).
+__device__ __forceinline__ bool moe_item(const int32_t* __restrict__ off, int E, int BM, int ntn, int& e_out,
+                                         int& r0_out, int& n_out, int& nt_out) {
+  int tiles = 0;
+  for (int e = 0; e < E; ++e) tiles += (off[e + 1] - off[e] + BM - 1) / BM;
+  const int n_real = tiles * ntn;
+  const int per = (n_real + 7) / 8;
+  const int k = (int)blockIdx.x / 8;
+  if (k >= per) return false;
+  int item = (int)(blockIdx.x % 8) * per + k;
+  if (item >= n_real) return false;
   for (int e = 0; e < E; ++e) {
     const int n = off[e + 1] - off[e];
-    const int nt = (n + BM - 1) / BM;
-    if (slot < cum + nt) {
+    const int mt = (n + BM - 1) / BM;
+    if (item < mt * ntn) {
       e_out = e;
-      r0_out = (slot - cum) * BM;
+      nt_out = item / mt;
+      r0_out = (item % mt) * BM;
       n_out = n;
       return true;
     }
-    cum += nt;
+    item -= mt * ntn;
   }
   return false;
 }
 
+// Grid for a grouped GEMM: an upper bound on the items, rounded to the 8 XCDs.
+static inline int moe_grid(int ntok, int E, int BM, int ntn) {
+  const int nmax = ((ntok + BM - 1) / BM + E) * ntn;
+  return 8 * ((nmax + 7) / 8);
+}
+
 template <typename T, int BM, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void moe_gateup_kernel(MoeArgs<T> a) {
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
   constexpr int BN = 128;  // 64 activation columns: gate and up in alternating 16-row blocks
   using Tile = GemmTile<T, BM, BN, WM, WN>;
   static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
-  int e, r0, n_e;
-  if (!find_tile(a.offsets, a.E, BM, blockIdx.y, e, r0, n_e)) return;
-  const int j = blockIdx.x;  // activation columns [64j, 64j + 64)
+  int e, r0, n_e, j;  // j: activation columns [64j, 64j + 64)
+  if (!moe_item(a.offsets, a.E, BM, a.I / 64, e, r0, n_e, j)) return;
   const int base = a.offsets[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
@@ -145,13 +164,14 @@ __global__ __launch_bounds__(WM* WN * 64) void moe_gateup_kernel(MoeArgs<T> a) {
 }
 
 template <typename T, int BM, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void moe_down_kernel(MoeArgs<T> a) {
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
   constexpr int BN = 128;
   using Tile = GemmTile<T, BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
-  int e, r0, n_e;
-  if (!find_tile(a.offsets, a.E, BM, blockIdx.y, e, r0, n_e)) return;
-  const int n0 = blockIdx.x * BN;
+  int e, r0, n_e, c;
+  if (!moe_item(a.offsets, a.E, BM, a.H / BN, e, r0, n_e, c)) return;
+  const int n0 = c * BN;
   const int base = a.offsets[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
@@ -185,20 +205,21 @@ __global__ __launch_bounds__(WM* WN * 64) void moe_down_kernel(MoeArgs<T> a) {
 
 template <typename T, int BM, int WM, int WN>
 static hipError_t launch_gateup_cfg(const MoeArgs<T>& a, hipStream_t s) {
-  const int slots = (a.ntok + BM - 1) / BM + a.E;
-  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN>), dim3(a.I / 64, slots), dim3(WM * WN * 64), 0, s, a);
+  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN>), dim3(moe_grid(a.ntok, a.E, BM, a.I / 64)),
+                     dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T, int BM, int WM, int WN>
 static hipError_t launch_down_cfg(const MoeArgs<T>& a, hipStream_t s) {
-  const int slots = (a.ntok + BM - 1) / BM + a.E;
-  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN>), dim3(a.H / 128, slots), dim3(WM * WN * 64), 0, s, a);
+  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN>), dim3(moe_grid(a.ntok, a.E, BM, a.H / 128)),
+                     dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
 
-// Row tile by load: 16-row tiles when experts see only a few tokens each (decode),
-// 128-row tiles otherwise.
+// Row tile by load: 16-row tiles when experts see only a few tokens each (decode);
+// otherwise 128-row tiles for gate/up and 64-row tiles for down (its K is the expert
+// width and its column tiles few, so smaller row tiles keep every CU busy).
 template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
@@ -210,7 +231,7 @@ template <typename T>
 hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
   if (a.ntok <= 32 * a.E) return launch_down_cfg<T, 16, 1, 4>(a, s);
-  return launch_down_cfg<T, 128, 2, 2>(a, s);
+  return launch_down_cfg<T, 64, 2, 2>(a, s);
 }
 
 template hipError_t launch_moe_gateup<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);
