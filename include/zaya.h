@@ -56,7 +56,7 @@ enum zaya_status {
 
 /* Block shape ("Config" and "Printout" on the nnterp page). Supported: head_dim in
  * {64, 128}; n_heads % n_kv_heads == 0 with n_heads / n_kv_heads in {1, 2, 4, 8};
- * rope_dim even and <= head_dim; conv_k == 3; n_experts + 1 <= 64; hidden a multiple
+ * rope_dim even and <= head_dim; conv_k == 3; n_experts + 1 <= 32; hidden a multiple
  * of 256 and <= 4096; expert_inter a multiple of 64; router_hidden == 256. */
 typedef struct zaya_block_config {
   int hidden;          /* H (hidden_size) */

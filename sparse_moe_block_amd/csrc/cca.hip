@@ -42,6 +42,9 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   T* xs = reinterpret_cast<T*>(cca_lds);
   float* wsm = reinterpret_cast<float*>(cca_lds + ((kCcaRows * ROWE * (int)sizeof(T) + 15) & ~15));
   // wsm[c*4 + 0..2] = conv taps of group channel c, wsm[c*4 + 3] = its bias
+  T* outs = reinterpret_cast<T*>(reinterpret_cast<char*>(wsm) + GC * 4 * sizeof(float));
+  // outs: per wave, the rows of the token(s) of one step (G query heads, key, value)
+  // gathered so they leave in 16-byte stores
   const int S = a.S, QR = a.qkv_ld;
   const int kcol = nh * d, vccol = nh * d + nkv * d, vdcol = vccol + nkv * d / 2;
   const int L0 = a.cache_len[b];
@@ -52,10 +55,22 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   // group channel c -> global channel (column of P, row of conv_w / conv_state)
   auto gchan = [&](int c) { return c < G * d ? g * G * d + c : kcol + g * d + (c - G * d); };
 
+  // the last token's normed input becomes prev_hs: requested now, stored at the end
+  constexpr int E16 = 16 / (int)sizeof(T);
+  const bool write_prev = t_end == S && g == 0;
+  const int prev_chunks = a.H / E16;
+  u32x4 prev[4];
+  if (write_prev) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * (int)blockDim.x;
+      if (i < prev_chunks) prev[k] = *reinterpret_cast<const u32x4*>(a.xn + ((size_t)b * S + S - 1) * a.H + i * E16);
+    }
+  }
+
   // 1. stage projection rows of tokens t0-2 .. t_end-1 (16-byte chunks of the four
   //    contiguous segments), and the history rows from conv_state / zeros
   {
-    constexpr int E16 = 16 / (int)sizeof(T);
     const int segq = G * d / E16, segk = d / E16, segv = (d / 2) / E16;
     const int per_row = segq + segk + 2 * segv;
     const int nrows = t_end - t0 + 2;
@@ -145,10 +160,8 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       cs = (float)cd;
       sn = (float)sd;
     }
-    const size_t row = (size_t)b * S + tt;
-    const size_t pos = (size_t)(L0 + tt);
+    T* ob = outs + (wave * tpw + sub) * (G + 2) * d;
     for (int hh = 0; hh < G; ++hh) {
-      const int h = g * G + hh;
       const float ss = group_sum(qa[hh] * qa[hh] + qb[hh] * qb[hh], spt);
       const float sc = sqrt_d / fmaxf(sqrtf(ss), 1e-12f);
       float va = qa[hh] * sc, vb = qb[hh] * sc;
@@ -157,16 +170,8 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         va = ra;
         vb = rb;
       }
-      if (active) {
-        T* qo = a.Q + (row * nh + h) * d;
-        qo[da] = Act<T>::cvt(va);
-        qo[db] = Act<T>::cvt(vb);
-        if (a.q_tap) {
-          T* qt = a.q_tap + (((size_t)b * nh + h) * S + tt) * d;
-          qt[da] = Act<T>::cvt(va);
-          qt[db] = Act<T>::cvt(vb);
-        }
-      }
+      ob[hh * d + da] = Act<T>::cvt(va);
+      ob[hh * d + db] = Act<T>::cvt(vb);
     }
     {
       const float ss = group_sum(ka * ka + kb * kb, spt);
@@ -180,25 +185,40 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       // values: current half of token t, delayed half of token t - 1
       auto vval = [&](int x) -> T { return x < d / 2 ? x0[GC + x] : x1[GC + x]; };
       const T vda = vval(da), vdb = vval(db);
-      if (active) {
-        T* ko = a.K + (((size_t)b * nkv + g) * a.cap + pos) * d;
-        T* vo = a.V + (((size_t)b * nkv + g) * a.cap + pos) * d;
-        ko[da] = Act<T>::cvt(va);
-        ko[db] = Act<T>::cvt(vb);
-        vo[da] = vda;
-        vo[db] = vdb;
-        if (a.k_tap) {
-          T* kt = a.k_tap + (((size_t)b * nkv + g) * S + tt) * d;
-          kt[da] = Act<T>::cvt(va);
-          kt[db] = Act<T>::cvt(vb);
+      ob[G * d + da] = Act<T>::cvt(va);
+      ob[G * d + db] = Act<T>::cvt(vb);
+      ob[(G + 1) * d + da] = vda;
+      ob[(G + 1) * d + db] = vdb;
+    }
+    // copy the step's rows out in 16-byte chunks (the wave's own LDS rows: LDS
+    // operations of one wave complete in order, so no barrier is needed)
+    __builtin_amdgcn_wave_barrier();
+    {
+      const int cpr = d / E16;             // chunks per row
+      const int cps = (G + 2) * cpr;       // chunks per token
+      for (int i = lane; i < tpw * cps; i += 64) {
+        const int sl = i / cps, q = i % cps, rw = q / cpr, ch = q % cpr;
+        const int t2 = base + sl;
+        if (t2 >= t_end) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(outs + ((wave * tpw + sl) * (G + 2) + rw) * d + ch * E16);
+        const size_t pos2 = (size_t)(L0 + t2);
+        T* dst;
+        T* tap;
+        if (rw < G) {
+          dst = a.Q + (((size_t)b * S + t2) * nh + g * G + rw) * d;
+          tap = a.q_tap ? a.q_tap + (((size_t)b * nh + g * G + rw) * S + t2) * d : nullptr;
+        } else if (rw == G) {
+          dst = a.K + (((size_t)b * nkv + g) * a.cap + pos2) * d;
+          tap = a.k_tap ? a.k_tap + (((size_t)b * nkv + g) * S + t2) * d : nullptr;
+        } else {
+          dst = a.V + (((size_t)b * nkv + g) * a.cap + pos2) * d;
+          tap = a.v_tap ? a.v_tap + (((size_t)b * nkv + g) * S + t2) * d : nullptr;
         }
-        if (a.v_tap) {
-          T* vt = a.v_tap + (((size_t)b * nkv + g) * S + tt) * d;
-          vt[da] = vda;
-          vt[db] = vdb;
-        }
+        *reinterpret_cast<u32x4*>(dst + ch * E16) = val;
+        if (tap) *reinterpret_cast<u32x4*>(tap + ch * E16) = val;
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 
   // 3. state for the next call. Only tile 0 reads the old conv_state (in step 1, before
@@ -209,23 +229,32 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
     for (int c = threadIdx.x; c < GC; c += blockDim.x) {
       const int gc = gchan(c);
       T* cs = a.conv_state + ((size_t)b * a.C + gc) * 2;
-      const T s0 = S >= 2 ? a.P[((size_t)b * S + S - 2) * QR + gc] : xs[1 * ROWE + c];
-      const T s1 = a.P[((size_t)b * S + S - 1) * QR + gc];
+      T s0, s1;
+      if (t_end == S) {  // one tile: rows S-2 (or the history row) and S-1 are in LDS
+        s0 = xs[S * ROWE + c];
+        s1 = xs[(S + 1) * ROWE + c];
+      } else {
+        s0 = a.P[((size_t)b * S + S - 2) * QR + gc];
+        s1 = a.P[((size_t)b * S + S - 1) * QR + gc];
+      }
       cs[0] = s0;
       cs[1] = s1;
     }
   }
-  if (t_end == S && g == 0) {
-    const T* src = a.xn + ((size_t)b * S + S - 1) * a.H;
-    T* dst = a.prev_hs + (size_t)b * a.H;
-    for (int i = threadIdx.x; i < a.H; i += blockDim.x) dst[i] = src[i];
+  if (write_prev) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * (int)blockDim.x;
+      if (i < prev_chunks) *reinterpret_cast<u32x4*>(a.prev_hs + (size_t)b * a.H + i * E16) = prev[k];
+    }
   }
 }
 
 size_t cca_lds_bytes(int d, int G, int act_bytes) {
   const int GC = (G + 1) * d;
   const size_t xs = ((size_t)kCcaRows * (GC + d) * act_bytes + 15) & ~(size_t)15;
-  return xs + (size_t)GC * 4 * sizeof(float);
+  const size_t outs = (size_t)4 * (128 / d) * (G + 2) * d * act_bytes;  // 4 waves x tokens per step
+  return xs + (size_t)GC * 4 * sizeof(float) + outs;
 }
 
 template <typename T>

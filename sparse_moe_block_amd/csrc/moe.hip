@@ -26,17 +26,37 @@ namespace zaya {
 
 // ----------------------------------------------------------------------------- buckets
 
+// One workgroup of 1024 threads. Tokens are taken in passes of up to kBucketPer
+// chunks of 1024 (chunk j: tokens pass0 + 1024 j + tid) whose classes are loaded at
+// once and kept in registers (up to 8192 tokens the second sweep reuses them). Counts
+// use LDS atomics; placement ranks each token among the same-expert tokens of its wave
+// with ballots and adds the counts of the earlier waves, chunk by chunk, so ids stay
+// ascending within an expert.
+constexpr int kBucketPer = 8;
+
 __global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict__ cls, int ntok, int E,
                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ ids) {
-  __shared__ int cnt[64];
-  __shared__ int base[64];
-  __shared__ int wcnt[16][64];
+  __shared__ int cnt[32];
+  __shared__ int base[32];
+  __shared__ int wcnt[16][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 64) cnt[tid] = 0;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const bool single = ntok <= kBucketPer * 1024;
+  int c[kBucketPer];
+  auto load = [&](int pass0) {
+#pragma unroll
+    for (int j = 0; j < kBucketPer; ++j) {
+      const int t = pass0 + j * 1024 + tid;
+      c[j] = t < ntok ? cls[t] : -1;
+    }
+  };
+  if (tid < 32) cnt[tid] = 0;
   __syncthreads();
-  for (int t = tid; t < ntok; t += blockDim.x) {
-    const int c = cls[t];
-    if (c >= 0 && c < E) atomicAdd(&cnt[c], 1);
+  for (int pass0 = 0; pass0 < ntok; pass0 += kBucketPer * 1024) {
+    load(pass0);
+#pragma unroll
+    for (int j = 0; j < kBucketPer; ++j)
+      if (c[j] >= 0 && c[j] < E) atomicAdd(&cnt[c[j]], 1);
   }
   __syncthreads();
   if (tid == 0) {
@@ -49,29 +69,32 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict_
     offsets[E] = run;
   }
   __syncthreads();
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int chunk = 0; chunk < ntok; chunk += blockDim.x) {
-    const int t = chunk + tid;
-    const int c = t < ntok ? cls[t] : -1;
-    int rank = 0;
-    for (int e = 0; e < E; ++e) {
-      const unsigned long long m = __ballot(c == e);
-      if (lane == 0) wcnt[wave][e] = __popcll(m);
-      if (c == e) rank = __popcll(m & lt);
+  for (int pass0 = 0; pass0 < ntok; pass0 += kBucketPer * 1024) {
+    if (!single) load(pass0);
+    const int nch = min(kBucketPer, (ntok - pass0 + 1023) / 1024);
+#pragma unroll
+    for (int j = 0; j < kBucketPer; ++j) {
+      if (j >= nch) break;
+      int rank = 0;
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long m = __ballot(c[j] == e);
+        if (lane == 0) wcnt[wave][e] = __popcll(m);
+        if (c[j] == e) rank = __popcll(m & lt);
+      }
+      __syncthreads();
+      if (c[j] >= 0 && c[j] < E) {
+        int pos = base[c[j]] + rank;
+        for (int w = 0; w < wave; ++w) pos += wcnt[w][c[j]];
+        ids[pos] = pass0 + j * 1024 + tid;
+      }
+      __syncthreads();
+      if (tid < E) {
+        int add = 0;
+        for (int w = 0; w < 16; ++w) add += wcnt[w][tid];
+        base[tid] += add;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (c >= 0 && c < E) {
-      int pos = base[c] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][c];
-      ids[pos] = t;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int add = 0;
-      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) add += wcnt[w][tid];
-      base[tid] += add;
-    }
-    __syncthreads();
   }
 }
 

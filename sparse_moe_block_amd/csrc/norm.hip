@@ -12,7 +12,7 @@ namespace zaya {
 
 // rows: number of rows; H % 256 == 0. Each lane owns H/256 groups of 4 consecutive
 // columns, strided 256 apart, so every wave-wide load is contiguous.
-template <typename T>
+template <typename T, int NG>
 __global__ __launch_bounds__(256) void rmsnorm_stream_kernel(const float* __restrict__ x, const T* __restrict__ g,
                                                                T* __restrict__ out, int rows, int H, float eps) {
   const int lane = threadIdx.x & 63;
@@ -20,14 +20,20 @@ __global__ __launch_bounds__(256) void rmsnorm_stream_kernel(const float* __rest
   if (row >= rows) return;
   const float* xr = x + (size_t)row * H;
   T* orow = out + (size_t)row * H;
-  constexpr int kMaxGroups = 16;  // H <= 4096
-  float v[kMaxGroups][4];
-  const int ng = H / 256;
+  constexpr int kMaxGroups = NG;  // H / 256 (compile time: registers for exactly this row)
+  float v[kMaxGroups][4], gv[kMaxGroups][4];
+  const int ng = NG;
+  // the row and the gain are requested together: one memory round trip per row
+#pragma unroll
+  for (int i = 0; i < kMaxGroups; ++i)
+    if (i < ng) {
+      load4(xr + i * 256 + lane * 4, v[i]);
+      load4(g + i * 256 + lane * 4, gv[i]);
+    }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxGroups; ++i) {
     if (i < ng) {
-      load4(xr + i * 256 + lane * 4, v[i]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         v[i][c] = Act<T>::rnd(v[i][c]);
@@ -40,10 +46,9 @@ __global__ __launch_bounds__(256) void rmsnorm_stream_kernel(const float* __rest
 #pragma unroll
   for (int i = 0; i < kMaxGroups; ++i) {
     if (i < ng) {
-      float gv[4], o[4];
-      load4(g + i * 256 + lane * 4, gv);
+      float o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(gv[c] * Act<T>::rnd(v[i][c] * inv));
+      for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(gv[i][c] * Act<T>::rnd(v[i][c] * inv));
       store4(orow + i * 256 + lane * 4, o);
     }
   }
@@ -75,7 +80,16 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 template <typename T>
 hipError_t launch_rmsnorm_stream(const float* x, const T* g, T* out, int rows, int H, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_stream_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, x, g, out, rows, H, eps);
+  const dim3 grid((rows + 3) / 4), block(256);
+  switch (H / 256) {  // H is a multiple of 256, at most 4096 (checked by the host)
+#define ZAYA_NORM_CASE(n) \
+  case n: hipLaunchKernelGGL((rmsnorm_stream_kernel<T, n>), grid, block, 0, s, x, g, out, rows, H, eps); break;
+    ZAYA_NORM_CASE(1) ZAYA_NORM_CASE(2) ZAYA_NORM_CASE(3) ZAYA_NORM_CASE(4) ZAYA_NORM_CASE(5) ZAYA_NORM_CASE(6)
+    ZAYA_NORM_CASE(7) ZAYA_NORM_CASE(8) ZAYA_NORM_CASE(9) ZAYA_NORM_CASE(10) ZAYA_NORM_CASE(11) ZAYA_NORM_CASE(12)
+    ZAYA_NORM_CASE(13) ZAYA_NORM_CASE(14) ZAYA_NORM_CASE(15) ZAYA_NORM_CASE(16)
+#undef ZAYA_NORM_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -13,8 +13,12 @@
 //   out = f32(f32(h + rb) * rs) + rnd(rnd(hsb) * hss),
 // which this kernel writes directly; routed tokens are written by the expert kernels.
 //
-// One workgroup of 4 waves per 16 tokens. fc1/fc2 run on MFMA with the weights read
-// straight from global memory (L2-resident: 2 x 128 KiB) and the activations in LDS.
+// One workgroup of 8 waves per 16 tokens. fc1, fc2 and out_proj run on MFMA with the
+// weight fragments read straight from global memory into registers (L2-resident:
+// 2 x 128 KiB + 8.5 KiB) and the activations in LDS. Every global read the kernel
+// makes (router state first, then biases, then weights) is issued at its start, so
+// the whole kernel waits for memory about once; the selection runs in registers, 16
+// lanes per token.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,193 +26,185 @@ namespace zaya {
 
 constexpr int kRouterTok = 16;
 constexpr int kRouterR = 256;
+constexpr int kRouterWaves = 8;
+constexpr int kRouterRows = kRouterR / kRouterWaves;  // fc output rows per wave
 
-// The wave's 64 weight rows of fc1 or fc2 (its whole K range) as MFMA fragments.
+// The wave's 32 weight rows of fc1 or fc2 (its whole K range) as MFMA fragments, and
+// the matching 8 bias values of this lane.
 template <typename T>
 struct RouterFcFrags {
-  typename Mfma<T>::frag f[4][kRouterR / 32];
+  typename Mfma<T>::frag f[kRouterRows / 16][kRouterR / 32];
+  float b[kRouterRows / 16][4];
+  __device__ __forceinline__ void load_bias(const T* __restrict__ bias) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int nb = 0; nb < kRouterRows / 16; ++nb) load4(bias + wave * kRouterRows + nb * 16 + (lane >> 4) * 4, b[nb]);
+  }
   __device__ __forceinline__ void load(const T* __restrict__ W) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < kRouterRows / 16; ++nb)
 #pragma unroll
       for (int ks = 0; ks < kRouterR / 32; ++ks)
-        f[nb][ks] = Mfma<T>::load(W + (size_t)(wave * 64 + nb * 16 + r16) * kRouterR + ks * 32 + grp * 8);
+        f[nb][ks] = Mfma<T>::load(W + (size_t)(wave * kRouterRows + nb * 16 + r16) * kRouterR + ks * 32 + grp * 8);
   }
 };
 
 template <typename T>
-__device__ __forceinline__ void router_fc(const RouterFcFrags<T>& W, const T* __restrict__ bias, const T* in_s,
-                                          T* out_s, int ldsrow) {
+__device__ __forceinline__ void router_fc(const RouterFcFrags<T>& W, const T* in_s, T* out_s, int ldsrow) {
   // out[t][n] = rnd(gelu(rnd(sum_k in[t][k] W[n][k] + b[n]))), t < 16, n < 256.
   using MF = Mfma<T>;
-  constexpr int KS = kRouterR / 32;
+  constexpr int KS = kRouterR / 32, NB = kRouterRows / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
-  const auto& wf = W.f;
-  f32x4 acc[4];
+  f32x4 acc[NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const typename MF::frag xf = MF::load(in_s + r16 * ldsrow + ks * 32 + grp * 8);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] = MF::mma(wf[nb][ks], xf, acc[nb]);
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = MF::mma(W.f[nb][ks], xf, acc[nb]);
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n0 = wave * 64 + nb * 16 + grp * 4;
-    float bb[4], v[4];
-    load4(bias + n0, bb);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n0 = wave * kRouterRows + nb * 16 + grp * 4;
+    float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x = Act<T>::rnd(acc[nb][i] + bb[i]);
+      const float x = Act<T>::rnd(acc[nb][i] + W.b[nb][i]);
       v[i] = Act<T>::rnd(0.5f * x * (1.0f + erff(x * 0.70710678118654752f)));
     }
     store4(out_s + r16 * ldsrow + n0, v);
   }
 }
 
+// Selection for one token: lanes 16 g .. 16 g + 15 of a wave hold the token's classes
+// c = lane % 16 and 16 + lane % 16. Softmax in fp64 over the fp32 logits (max and sum by
+// shuffles inside the 16-lane group), probabilities rounded to fp32, plus the balancing
+// biases in fp32; the first (lowest-index) maximum wins.
+__device__ __forceinline__ double group16_max(double v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 16));
+  return v;
+}
+__device__ __forceinline__ double group16_sum(double v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+  return v;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs<T> a) {
+__global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T> a) {
   constexpr int ROW = kRouterR + 16 / (int)sizeof(T);  // padded LDS row (elements)
   __shared__ __attribute__((aligned(16))) T z_s[kRouterTok * ROW];
   __shared__ __attribute__((aligned(16))) T a1_s[kRouterTok * ROW];
   __shared__ __attribute__((aligned(16))) T a2_s[kRouterTok * ROW];
-  __shared__ float lg_s[kRouterTok][64];
+  __shared__ float lg_s[kRouterTok][33];
   __shared__ int cls_s[kRouterTok];
-  __shared__ double ex_s[kRouterTok][64];
-  __shared__ double mx_s[kRouterTok];
-  __shared__ float bb_s[64];
-  __shared__ __attribute__((aligned(16))) T wout_s[64 * ROW];  // out_proj rows, staged once
 
   const int tok0 = blockIdx.x * kRouterTok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
   const int E = a.E, NC = a.E + 1;
 
-  // Every global tensor this kernel reads is first touched here, together, so the
-  // memory round trips (and address-translation walks) of its phases overlap instead
-  // of queueing one phase after another: fc1's weight fragments go straight into
-  // registers, fc2's and the skip-merge parameters are touched with one load each.
-  RouterFcFrags<T> w1;
+  // All global reads, in the order they are needed: the router state rows (wave w
+  // normalizes tokens 2w, 2w+1; lane owns 4 consecutive values) and the norm gain, the
+  // biases and balancing biases, then the weight fragments of fc1, fc2 and out_proj
+  // (waves 0 and 1: classes 16 w .. 16 w + 15; rows past the last class repeat it and
+  // are discarded).
+  float v[2][4], g[4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tok = tok0 + wave * 2 + tt;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[tt][c] = 0.f;
+    if (tok < a.ntok) load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
+  }
+  load4(a.norm_g + lane * 4, g);
+  RouterFcFrags<T> w1, w2;
+  w1.load_bias(a.b1);
+  w2.load_bias(a.b2);
+  const float bb1 = r16 < NC ? a.bal_bias[r16] : 0.f;
+  const float bb2 = 16 + r16 < NC ? a.bal_bias[16 + r16] : 0.f;
   w1.load(a.W1);
-  {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const T* touch[] = {a.W2 + (size_t)(wave * 64 + lane) * kRouterR, a.b1, a.b2, a.norm_g, a.m_hsb, a.m_hss,
-                        a.m_rb, a.m_rs};
-    uint32_t acc = 0;
+  if constexpr (sizeof(T) == 2) w2.load(a.W2);  // fp32 fragments are twice the size: loaded after fc1
+  typename Mfma<T>::frag wo[kRouterR / 32];
+  if (wave < 2) {
+    const int c = min(wave * 16 + r16, NC - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc += *reinterpret_cast<const volatile uint16_t*>(touch[i]);
-    if (acc == 0xFFFFFFFFu) a.cls[0] = -1;  // never true: keeps the touches alive
+    for (int ks = 0; ks < kRouterR / 32; ++ks)
+      wo[ks] = Mfma<T>::load(a.Wout + (size_t)c * kRouterR + ks * 32 + grp * 8);
   }
-  // stage out_proj (E+1 rows of R) and the balancing biases in LDS
-  if (threadIdx.x < NC) bb_s[threadIdx.x] = a.bal_bias[threadIdx.x];
-  {
-    constexpr int E16 = 16 / (int)sizeof(T);
-    const int nchunk = NC * (kRouterR / E16);
-    for (int ch = threadIdx.x; ch < nchunk; ch += blockDim.x) {
-      const int r = ch / (kRouterR / E16), col = (ch % (kRouterR / E16)) * E16;
-      *reinterpret_cast<uint4*>(wout_s + r * ROW + col) =
-          *reinterpret_cast<const uint4*>(a.Wout + (size_t)r * kRouterR + col);
-    }
-  }
-  // RMSNorm of u: wave w handles tokens 4w..4w+3, lane owns 4 consecutive values; the
-  // four rows are loaded together
-  {
-    float v[4][4], g[4];
+
+  // RMSNorm of u
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = tok0 + wave * 4 + tt;
+  for (int tt = 0; tt < 2; ++tt) {
+    float ss = v[tt][0] * v[tt][0] + v[tt][1] * v[tt][1] + v[tt][2] * v[tt][2] + v[tt][3] * v[tt][3];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)kRouterR + a.eps);
+    float o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[tt][c] = 0.f;
-      if (tok < a.ntok) load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
-    }
-    load4(a.norm_g + lane * 4, g);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      float ss = v[tt][0] * v[tt][0] + v[tt][1] * v[tt][1] + v[tt][2] * v[tt][2] + v[tt][3] * v[tt][3];
-      ss = wave_sum(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)kRouterR + a.eps);
-      float o[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(g[c] * Act<T>::rnd(v[tt][c] * inv));
-      store4(z_s + (wave * 4 + tt) * ROW + lane * 4, o);
-    }
+    for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(g[c] * Act<T>::rnd(v[tt][c] * inv));
+    store4(z_s + (wave * 2 + tt) * ROW + lane * 4, o);
   }
   __syncthreads();
-  router_fc<T>(w1, a.b1, z_s, a1_s, ROW);
-  RouterFcFrags<T> w2;
-  w2.load(a.W2);
+  router_fc<T>(w1, z_s, a1_s, ROW);
+  if constexpr (sizeof(T) == 4) w2.load(a.W2);
   __syncthreads();
-  router_fc<T>(w2, a.b2, a1_s, a2_s, ROW);
+  router_fc<T>(w2, a1_s, a2_s, ROW);
   __syncthreads();
 
-  // out_proj: (token, class) pairs
-  for (int task = threadIdx.x; task < kRouterTok * NC; task += blockDim.x) {
-    const int t = task / NC, c = task % NC;
-    const T* wr = wout_s + c * ROW;
-    const T* xr = a2_s + t * ROW;
-    float acc = 0.f;
-    for (int k = 0; k < kRouterR; k += 4) {
-      float wv[4], xv[4];
-      load4(wr + k, wv);
-      load4(xr + k, xv);
-      acc += wv[0] * xv[0] + wv[1] * xv[1] + wv[2] * xv[2] + wv[3] * xv[3];
+  // out_proj on MFMA: logits[t][c] = rnd(sum_k a2[t][k] Wout[c][k]), waves 0 and 1
+  if (wave < 2) {
+    using MF = Mfma<T>;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kRouterR / 32; ++ks)
+      acc = MF::mma(wo[ks], MF::load(a2_s + r16 * ROW + ks * 32 + grp * 8), acc);
+    // lane holds classes 16 w + 4 grp + i of token r16
+    const int tok = tok0 + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = wave * 16 + grp * 4 + i;
+      const float l = Act<T>::rnd(acc[i]);
+      lg_s[r16][c] = l;
+      if (c < NC && tok < a.ntok) a.logits[(size_t)tok * NC + c] = Act<T>::cvt(l);
     }
-    const float l = Act<T>::rnd(acc);
-    lg_s[t][c] = l;
-    const int tok = tok0 + t;
-    if (tok < a.ntok) a.logits[(size_t)tok * NC + c] = Act<T>::cvt(l);
   }
   __syncthreads();
 
-  // selection: softmax over the fp32 logits in double, rounded to fp32 (the exponentials
-  // and quotients of all (token, class) pairs in parallel), plus the balancing biases
-  // in fp32, first argmax
-  if (threadIdx.x < kRouterTok) {
-    const int t = threadIdx.x;
-    double mx = -INFINITY;
-    for (int c = 0; c < NC; ++c) mx = fmax(mx, (double)lg_s[t][c]);
-    mx_s[t] = mx;
-  }
-  __syncthreads();
-  for (int task = threadIdx.x; task < kRouterTok * NC; task += blockDim.x) {
-    const int t = task / NC, c = task % NC;
-    ex_s[t][c] = exp((double)lg_s[t][c] - mx_s[t]);
-  }
-  __syncthreads();
-  if (threadIdx.x < kRouterTok) {
-    const int t = threadIdx.x;
-    double sum = 0.0;
-    for (int c = 0; c < NC; ++c) sum += ex_s[t][c];
-    mx_s[t] = sum;
-  }
-  __syncthreads();
-  for (int task = threadIdx.x; task < kRouterTok * NC; task += blockDim.x) {
-    const int t = task / NC, c = task % NC;
-    lg_s[t][c] = (float)(ex_s[t][c] / mx_s[t]);  // probabilities replace the logits
-  }
-  __syncthreads();
-  if (threadIdx.x < kRouterTok) {
-    const int t = threadIdx.x, tok = tok0 + t;
-    int best = 0;
-    float best_s = -INFINITY, best_p = 0.f;
-    for (int c = 0; c < NC; ++c) {
-      const float p = lg_s[t][c];
-      const float sg = p + bb_s[c];
-      if (sg > best_s) {
-        best_s = sg;
-        best = c;
-        best_p = p;
+  // selection: waves 0..3, wave w handles tokens 4 w .. 4 w + 3, one per 16-lane group
+  if (wave < 4) {
+    const int t = wave * 4 + grp, tok = tok0 + t;
+    const int c1 = r16, c2 = 16 + r16;
+    const bool has1 = c1 < NC, has2 = c2 < NC;  // classes past E are padding
+    const double l1 = has1 ? (double)lg_s[t][c1] : -INFINITY, l2 = has2 ? (double)lg_s[t][c2] : -INFINITY;
+    const double mx = group16_max(fmax(l1, l2));
+    const double e1 = has1 ? exp(l1 - mx) : 0.0, e2 = has2 ? exp(l2 - mx) : 0.0;
+    const double sum = group16_sum(e1 + e2);
+    const float p1 = (float)(e1 / sum), p2 = (float)(e2 / sum);
+    const float s1 = has1 ? p1 + bb1 : -INFINITY;
+    const float s2 = has2 ? p2 + bb2 : -INFINITY;
+    // best of this lane's two (c1 < c2: c2 wins only if strictly larger)
+    float bs = s1, bp = p1;
+    int bc = c1;
+    if (s2 > s1) { bs = s2; bp = p2; bc = c2; }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      const float os = __shfl_xor(bs, o, 16), op = __shfl_xor(bp, o, 16);
+      const int oc = __shfl_xor(bc, o, 16);
+      if (os > bs || (os == bs && oc < bc)) { bs = os; bp = op; bc = oc; }
+    }
+    if (r16 == 0) {
+      cls_s[t] = bc;
+      if (tok < a.ntok) {
+        const bool skip = bc == E;
+        a.cls[tok] = bc;
+        a.idx[tok] = skip ? 0 : bc;
+        a.wts[tok] = Act<T>::cvt(skip ? 0.f : bp);
       }
-    }
-    cls_s[t] = best;
-    if (tok < a.ntok) {
-      const bool skip = best == E;
-      a.cls[tok] = best;
-      a.idx[tok] = skip ? 0 : best;
-      a.wts[tok] = Act<T>::cvt(skip ? 0.f : best_p);
     }
   }
   __syncthreads();
@@ -242,7 +238,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs<T> a) {
 template <typename T>
 hipError_t launch_router(const RouterArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_kernel<T>, dim3((a.ntok + kRouterTok - 1) / kRouterTok), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(router_kernel<T>, dim3((a.ntok + kRouterTok - 1) / kRouterTok), dim3(kRouterWaves * 64), 0, s,
+                     a);
   return hipGetLastError();
 }
 

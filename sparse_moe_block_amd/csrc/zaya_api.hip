@@ -50,7 +50,7 @@ int check_config(const zaya_block_config* c) {
   if (c->rope_dim < 0 || c->rope_dim > c->head_dim || (c->rope_dim & 1))
     return fail(ZAYA_ESHAPE, "rope_dim %d must be even and <= head_dim", c->rope_dim);
   if (c->conv_k != 3) return fail(ZAYA_ESHAPE, "conv_k %d != 3", c->conv_k);
-  if (c->n_experts + 1 > 64) return fail(ZAYA_ESHAPE, "n_experts + 1 > 64");
+  if (c->n_experts + 1 > 32) return fail(ZAYA_ESHAPE, "n_experts + 1 > 32");
   if (c->hidden % 256 || c->hidden > 4096) return fail(ZAYA_ESHAPE, "hidden %d must be a multiple of 256, <= 4096", c->hidden);
   if (c->expert_inter % 64) return fail(ZAYA_ESHAPE, "expert_inter %d must be a multiple of 64", c->expert_inter);
   if (c->router_hidden != 256) return fail(ZAYA_ESHAPE, "router_hidden %d != 256", c->router_hidden);

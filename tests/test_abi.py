@@ -80,7 +80,7 @@ BAD_CONFIGS = [
     (dict(rope_dim=63), -2, "rope_dim"),
     (dict(rope_dim=256), -2, "rope_dim"),
     (dict(conv_k=2), -2, "conv_k"),
-    (dict(num_experts=64), -2, "n_experts"),
+    (dict(num_experts=32), -2, "n_experts"),
     (dict(hidden_size=2000), -2, "hidden"),
     (dict(moe_intermediate_size=2000), -2, "expert_inter"),
     (dict(router_hidden=128), -2, "router_hidden"),
