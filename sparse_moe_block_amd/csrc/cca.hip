@@ -32,11 +32,14 @@ constexpr int kCcaRows = kCcaTokens + 2;  // the tile plus two tokens of history
 //   xs[r][G*d .. (G+1)*d)  k channels of the group's key head
 //   xs[r][(G+1)*d .. +d/2) v_current half of the group
 //   xs[r][.. +d/2)          v_delayed half of the group
-template <typename T>
+// D (head_dim) and GG (query heads per KV head) are compile-time, so the per-head
+// loops unroll and the head norms' cross-lane reductions run side by side.
+template <typename T, int D, int GG>
 __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   extern __shared__ __attribute__((aligned(16))) char cca_lds[];
   const int b = blockIdx.z, g = blockIdx.y, tile = blockIdx.x;
-  const int d = a.d, nh = a.nh, nkv = a.nkv, G = nh / nkv, r = a.rope_dim;
+  constexpr int d = D, G = GG;
+  const int nh = a.nh, nkv = a.nkv, r = a.rope_dim;
   const int GC = (G + 1) * d;          // q and k channels of the group
   const int ROWE = GC + d;             // + both value halves
   T* xs = reinterpret_cast<T*>(cca_lds);
@@ -69,15 +72,16 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   }
 
   // 1. stage projection rows of tokens t0-2 .. t_end-1 (16-byte chunks of the four
-  //    contiguous segments), and the history rows from conv_state / zeros
+  //    contiguous segments), the history rows from conv_state / zeros, and the conv
+  //    taps. Each loop issues its loads in batches of kBatch per thread before any of
+  //    them is stored, so the tile waits for memory a few times, not once per chunk.
   {
+    constexpr int kBatch = 8;
+    const int nthr = (int)blockDim.x;
     const int segq = G * d / E16, segk = d / E16, segv = (d / 2) / E16;
     const int per_row = segq + segk + 2 * segv;
     const int nrows = t_end - t0 + 2;
-    for (int ch = threadIdx.x; ch < nrows * per_row; ch += blockDim.x) {
-      const int rr = ch / per_row, cc = ch % per_row;
-      const int t = t0 - 2 + rr;
-      int src, dst;
+    auto chunk_cols = [&](int cc, int& src, int& dst) {
       if (cc < segq) {
         src = g * G * d + cc * E16;
         dst = cc * E16;
@@ -91,35 +95,73 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         src = vdcol + g * (d / 2) + (cc - segq - segk - segv) * E16;
         dst = GC + d / 2 + (cc - segq - segk - segv) * E16;
       }
-      if (t >= 0)  // rows before the sequence start are the history, filled below
-        *reinterpret_cast<uint4*>(xs + rr * ROWE + dst) =
-            *reinterpret_cast<const uint4*>(a.P + ((size_t)b * S + t) * QR + src);
+    };
+    for (int c0 = threadIdx.x; c0 < nrows * per_row; c0 += kBatch * nthr) {
+      u32x4 val[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int ch = c0 + k * nthr;
+        const int rr = ch / per_row, t = t0 - 2 + rr;
+        int src, dst;
+        chunk_cols(ch % per_row, src, dst);
+        if (ch < nrows * per_row && t >= 0)  // rows before the sequence start are the history
+          val[k] = *reinterpret_cast<const u32x4*>(a.P + ((size_t)b * S + t) * QR + src);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int ch = c0 + k * nthr;
+        const int rr = ch / per_row, t = t0 - 2 + rr;
+        int src, dst;
+        chunk_cols(ch % per_row, src, dst);
+        if (ch < nrows * per_row && t >= 0) *reinterpret_cast<u32x4*>(xs + rr * ROWE + dst) = val[k];
+      }
     }
     // history (tokens -2, -1 of a sequence with cached tokens): q/k channels from
     // conv_state, the delayed value from prev_hs @ W_vd^T
     if (t0 == 0) {
-      for (int i = threadIdx.x; i < 2 * GC; i += blockDim.x) {
-        const int rr = i / GC, c = i % GC;
-        const T v = fresh ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + rr];
-        xs[rr * ROWE + c] = v;
+      for (int i0 = threadIdx.x; i0 < 2 * GC; i0 += kBatch * nthr) {
+        T hv[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int i = i0 + k * nthr;
+          const int rr = i / GC, c = i % GC;
+          hv[k] = (fresh || i >= 2 * GC) ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + rr];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int i = i0 + k * nthr;
+          if (i < 2 * GC) xs[(i / GC) * ROWE + i % GC] = hv[k];
+        }
       }
-      for (int i = threadIdx.x; i < d / 2; i += blockDim.x)
+      for (int i = threadIdx.x; i < d / 2; i += nthr)
         xs[1 * ROWE + GC + d / 2 + i] =
             fresh ? Act<T>::cvt(0.f) : a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + i];
     }
-    for (int c = threadIdx.x; c < GC; c += blockDim.x) {
-      const int gc = gchan(c);
-      wsm[c * 4 + 0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
-      wsm[c * 4 + 1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
-      wsm[c * 4 + 2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
-      wsm[c * 4 + 3] = Act<T>::tof(a.conv_b[gc]);
+    for (int c0 = threadIdx.x; c0 < GC; c0 += 2 * nthr) {
+      float wv[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = c0 + k * nthr;
+        const int gc = gchan(min(c, GC - 1));
+        wv[k][0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
+        wv[k][1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
+        wv[k][2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
+        wv[k][3] = Act<T>::tof(a.conv_b[gc]);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = c0 + k * nthr;
+        if (c < GC)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wsm[c * 4 + q] = wv[k][q];
+      }
     }
   }
   __syncthreads();
 
   // 2. compute: lane p owns the dim pair (da, db) of every head of the group
-  const int spt = d / 2;     // lanes per token
-  const int tpw = 64 / spt;  // tokens per wave step
+  constexpr int spt = d / 2;     // lanes per token
+  constexpr int tpw = 64 / spt;  // tokens per wave step
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / spt, p = lane % spt;
   const int da = p < r / 2 ? p : r + (p - r / 2);
@@ -141,8 +183,9 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
     };
     const int kca = G * d + da, kcb = G * d + db;
     const float pka = Act<T>::tof(x0[kca]), pkb = Act<T>::tof(x0[kcb]);
-    float qa[8], qb[8];
+    float qa[G], qb[G];
     float rka = 0.f, rkb = 0.f;
+#pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const int ca = hh * d + da, cb = hh * d + db;
       const float rqa = (Act<T>::tof(x0[ca]) + pka) * 0.5f, rqb = (Act<T>::tof(x0[cb]) + pkb) * 0.5f;
@@ -161,9 +204,18 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       sn = (float)sd;
     }
     T* ob = outs + (wave * tpw + sub) * (G + 2) * d;
+    // squared lengths of the G query heads and the key head, reduced together
+    float ss[G + 1];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) ss[hh] = qa[hh] * qa[hh] + qb[hh] * qb[hh];
+    ss[G] = ka * ka + kb * kb;
+#pragma unroll
+    for (int o = spt / 2; o > 0; o >>= 1)
+#pragma unroll
+      for (int i = 0; i <= G; ++i) ss[i] += __shfl_xor(ss[i], o, 64);
+#pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float ss = group_sum(qa[hh] * qa[hh] + qb[hh] * qb[hh], spt);
-      const float sc = sqrt_d / fmaxf(sqrtf(ss), 1e-12f);
+      const float sc = sqrt_d / fmaxf(sqrtf(ss[hh]), 1e-12f);
       float va = qa[hh] * sc, vb = qb[hh] * sc;
       if (p < r / 2) {
         const float ra = va * cs - vb * sn, rb = vb * cs + va * sn;
@@ -174,8 +226,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       ob[hh * d + db] = Act<T>::cvt(vb);
     }
     {
-      const float ss = group_sum(ka * ka + kb * kb, spt);
-      const float sc = temp * sqrt_d / fmaxf(sqrtf(ss), 1e-12f);
+      const float sc = temp * sqrt_d / fmaxf(sqrtf(ss[G]), 1e-12f);
       float va = ka * sc, vb = kb * sc;
       if (p < r / 2) {
         const float ra = va * cs - vb * sn, rb = vb * cs + va * sn;
@@ -260,9 +311,17 @@ size_t cca_lds_bytes(int d, int G, int act_bytes) {
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s) {
   dim3 grid((a.S + kCcaTokens - 1) / kCcaTokens, a.nkv, a.B);
-  const size_t lds = cca_lds_bytes(a.d, a.nh / a.nkv, (int)sizeof(T));
-  hipLaunchKernelGGL(cca_kernel<T>, grid, dim3(256), lds, s, a);
-  return hipGetLastError();
+  const int G = a.nh / a.nkv;
+  const size_t lds = cca_lds_bytes(a.d, G, (int)sizeof(T));
+#define ZAYA_CCA_CASE(DD, GG)                                                      \
+  if (a.d == DD && G == GG) {                                                      \
+    hipLaunchKernelGGL((cca_kernel<T, DD, GG>), grid, dim3(256), lds, s, a);        \
+    return hipGetLastError();                                                      \
+  }
+  ZAYA_CCA_CASE(128, 1) ZAYA_CCA_CASE(128, 2) ZAYA_CCA_CASE(128, 4) ZAYA_CCA_CASE(128, 8)
+  ZAYA_CCA_CASE(64, 1) ZAYA_CCA_CASE(64, 2) ZAYA_CCA_CASE(64, 4) ZAYA_CCA_CASE(64, 8)
+#undef ZAYA_CCA_CASE
+  return hipErrorInvalidValue;
 }
 
 template hipError_t launch_cca<bf16_t>(const CcaArgs<bf16_t>&, hipStream_t);
