@@ -136,15 +136,19 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
   epi(i / N, i % N, v);
 }
 
-// Tile choice by grid size: the largest tile that still gives about one workgroup per
-// CU or more; GEMMs with at most 64 rows split K instead (they stream weights).
+// Tile choice. GEMMs with few rows (decode) split K into parts reduced by a second
+// pass (they stream weights). Otherwise the tile is picked by a cost model: a CU runs two 128-row tiles at once,
+// so the cost of a tile shape is (rounds of 512 tiles) x (tile area); 128x96 wins when
+// it fills the rounds that 128x128 leaves partly empty (N = 1536: 512 tiles instead of
+// 384). Small grids use 64x64 or 32x64 tiles.
 template <typename T, class Epi>
 static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, int N, int K, Epi epi, float* part,
                              size_t part_bytes, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   constexpr int kBK = 128 / (int)sizeof(T);
+  const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
   if (M <= 64 && part) {
-    const int ntiles = (N + 63) / 64;
+    const int ntiles = (int)t64;
     int kparts = 1;
     while (ntiles * kparts * 2 <= 512 && (K / kBK) / (kparts * 2) >= 4 &&
            (size_t)M * N * kparts * 2 * sizeof(float) <= part_bytes)
@@ -160,8 +164,12 @@ static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, in
     }
   }
   const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
-  if (t128 >= 240) return launch_cfg<T, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
+  const long t96 = (long)((M + 127) / 128) * ((N + 95) / 96);
+  if (t128 >= 240) {
+    const long c128 = (t128 + 511) / 512 * 128, c96 = (t96 + 511) / 512 * 96;
+    if (c96 < c128) return launch_cfg<T, 128, 96, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
+    return launch_cfg<T, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
+  }
   if (t64 >= 120) return launch_cfg<T, 64, 64, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
   return launch_cfg<T, 32, 64, 1, 4>(A, lda, B, ldb, M, N, K, epi, s);
 }

@@ -35,9 +35,9 @@ struct GemmTile {
   static constexpr int kBufBytes = (BM + BN) * kRowBytes;
   static constexpr int kLdsBytes = 2 * kBufBytes;
   // Waves per SIMD the kernel is compiled for (register budget 512 / waves): 2 for the
-  // 128x128 tiles (64 KiB of LDS already allows only two workgroups per CU), more for
-  // the smaller ones.
-  static constexpr int kWavesPerEU = BM * BN >= 128 * 128 ? 2 : 4;
+  // 128x96 and 128x128 tiles (their LDS already allows only two workgroups per CU), 4
+  // for the smaller ones.
+  static constexpr int kWavesPerEU = BM * BN >= 128 * 96 ? 2 : 4;
   static_assert(BM % (WM * 16) == 0 && BN % (WN * 16) == 0, "tile must split into 16x16 blocks");
   static_assert(kKSteps >= 1, "slice too short");
 
