@@ -237,6 +237,32 @@ def time_steps(setup: Setup, steps: int, warmup: int, hip: _Hip):
     return ms, wall
 
 
+def time_graph(setup: Setup, steps: int, warmup: int, hip: _Hip):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed:
+    the launch sequence is fixed, so the replays time the kernels without per-call host
+    work. Returns ms per replay."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        setup.step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed(e0, e1) / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    del g
+    return ms
+
+
 def time_stages(setup: Setup, steps: int, hip: _Hip):
     """Per-stage durations (ms, averaged over steps) from events recorded by the library
     on the launch stream between its kernels."""
@@ -262,6 +288,7 @@ def measure(cfg, steps, warmup, hip):
     setup = Setup(cfg)
     n_routed, n_used, counts = setup.routing()
     ms, wall = time_steps(setup, steps, warmup, hip)
+    graph_ms = time_graph(setup, steps, warmup, hip) if cfg.decode else None
     stages = time_stages(setup, steps, hip)
     work = stage_work(cfg, n_routed, n_used)
     table = {}
@@ -278,7 +305,7 @@ def measure(cfg, steps, warmup, hip):
     total_b = sum(v[1] for v in work.values())
     del setup
     torch.cuda.empty_cache()
-    return {"ms": ms, "wall": wall, "stages": table, "roofline": roof, "n_routed": n_routed, "experts_used": n_used,
+    return {"ms": ms, "graph_ms": graph_ms, "wall": wall, "stages": table, "roofline": roof, "n_routed": n_routed, "experts_used": n_used,
             "expert_counts": counts, "step_gflop": total_f / 1e9, "step_mbytes": total_b / 1e6}
 
 
@@ -338,7 +365,8 @@ def main():
     if not args.no_decode:
         dcfg = CONFIGS["decode"]
         dec = measure(dcfg, args.steps, args.warmup, hip)
-        print(f"[bench] decode {dec['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+        print(f"[bench] decode {dec['ms']:.4f} ms/step, {dec['graph_ms']:.4f} ms/step as a graph replay",
+              file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(pcfg)
     T = pcfg.tokens
     value = T / (pre["ms"] * 1e-3)
@@ -362,7 +390,9 @@ def main():
         line["decode"] = {"tok_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "ms_per_step": round(dec["ms"], 5),
                           "step_mbytes": round(dec["step_mbytes"], 1),
                           "frac_of_hbm_peak": round(dec["step_mbytes"] / (dec["ms"] * 1e-3) / 1e3 / PEAK_HBM_GBS, 4),
-                          "experts_used": dec["experts_used"], "roofline": dec["roofline"], "stages": dec["stages"]}
+                          "experts_used": dec["experts_used"], "roofline": dec["roofline"], "stages": dec["stages"],
+                          "graph": {"ms_per_step": round(dec["graph_ms"], 5),
+                                    "tok_s": round(dcfg.batch / (dec["graph_ms"] * 1e-3), 1)}}
     print(json.dumps(line))
 
 

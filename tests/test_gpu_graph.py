@@ -1,0 +1,104 @@
+"""A multi-block decode step captured in a HIP graph (through torch.cuda.CUDAGraph) gives
+bit-identical results to the same calls made eagerly, on every replay.
+
+The library allocates nothing and launches only kernels and device-to-device copies on
+the caller's stream, with every host-side decision taken from the call's arguments, so
+a captured step replays exactly what the eager step ran. Replays are interleaved with
+unrelated eager GPU work and synchronisations, and each replay starts from the same
+cache state (the step writes K/V at position cache_len and updates conv_state and
+prev_hs in place), so each must reproduce the eager outputs bit for bit."""
+import pytest
+import torch
+
+import sparse_moe_block_amd as Z
+from tests.zaya_harness import DEV
+from zaya_synth import CONFIGS, _device_stream, block_weights_device
+
+pytestmark = pytest.mark.gpu
+
+L_BLOCKS = 4
+
+
+def _caches(cfg, n_blocks):
+    B, nkv, d, H, C = cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.hidden_size, cfg.conv_channels
+    cap = cfg.kv_len + 1
+    out = []
+    for l in range(n_blocks):
+        def rnd(name, shape):
+            g = _device_stream(0, cfg.name + "_graph", l, name, DEV)
+            return torch.randn(shape, generator=g, device=DEV).to(cfg.torch_dtype)
+        K = torch.zeros((B, nkv, cap, d), device=DEV, dtype=cfg.torch_dtype)
+        V = torch.zeros_like(K)
+        K[:, :, :cfg.kv_len] = rnd("K", (B, nkv, cfg.kv_len, d))
+        V[:, :, :cfg.kv_len] = rnd("V", (B, nkv, cfg.kv_len, d))
+        out.append({"K": K, "V": V, "conv_state": rnd("conv", (B, C, 2)), "prev_hs": rnd("prev", (B, H)),
+                    "cache_len": [cfg.kv_len] * B,
+                    "cache_len_dev": torch.full((B,), cfg.kv_len, dtype=torch.int32, device=DEV)})
+    return out
+
+
+def test_graph_captured_decode_step_is_bit_identical_to_eager():
+    cfg = CONFIGS["decode"]
+    B, H, R = cfg.batch, cfg.hidden_size, cfg.router_hidden
+    blocks = [block_weights_device(cfg, l) for l in range(L_BLOCKS)]
+    caches = _caches(cfg, L_BLOCKS)
+    pos = cfg.kv_len
+    g0 = _device_stream(0, cfg.name + "_graph", -1, "x", DEV)
+    xs = [torch.randn((B, H), generator=g0, device=DEV)] + [torch.empty((B, H), device=DEV) for _ in range(L_BLOCKS)]
+    ss = [torch.randn((B, R), generator=g0, device=DEV).to(cfg.torch_dtype)] + \
+         [torch.empty((B, R), device=DEV, dtype=cfg.torch_dtype) for _ in range(L_BLOCKS)]
+    ws = torch.empty(Z.zaya_block_workspace_bytes(cfg, B, 1, True), dtype=torch.uint8, device=DEV)
+    pristine = [{k: c[k].clone() for k in ("conv_state", "prev_hs")} for c in caches]
+
+    def restore():
+        for c, p in zip(caches, pristine):
+            c["conv_state"].copy_(p["conv_state"])
+            c["prev_hs"].copy_(p["prev_hs"])
+            c["K"][:, :, pos].zero_()
+            c["V"][:, :, pos].zero_()
+        for t in xs[1:]:
+            t.fill_(float("nan"))
+        for t in ss[1:]:
+            t.fill_(float("nan"))
+
+    def step():
+        for l in range(L_BLOCKS):
+            Z.zaya_block_decode(cfg, blocks[l], B, xs[l], ss[l], xs[l + 1], ss[l + 1], caches[l], workspace=ws)
+
+    def snapshot():
+        out = {f"x{l}": xs[l + 1].clone() for l in range(L_BLOCKS)}
+        out.update({f"s{l}": ss[l + 1].clone() for l in range(L_BLOCKS)})
+        for l, c in enumerate(caches):
+            out[f"conv{l}"] = c["conv_state"].clone()
+            out[f"prev{l}"] = c["prev_hs"].clone()
+            out[f"K{l}"] = c["K"][:, :, pos].clone()
+            out[f"V{l}"] = c["V"][:, :, pos].clone()
+        return out
+
+    restore()
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot()
+    assert all(torch.isfinite(v.float()).all() for v in eager.values())
+
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        # unrelated eager work between replays
+        a = torch.randn((512, 512), device=DEV)
+        (a @ a).sum().item()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for k, v in eager.items():
+            assert torch.equal(v.view(torch.uint8) if v.dtype != torch.float32 else v.view(torch.int32),
+                               got[k].view(torch.uint8) if v.dtype != torch.float32 else got[k].view(torch.int32)), \
+                f"replay {rep}: {k} differs from the eager step"
+        print(f"replay {rep}: {len(eager)} tensors bit-identical", flush=True)
