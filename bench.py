@@ -160,8 +160,12 @@ def stage_work(cfg, n_routed: int, n_used: int):
     out["router_mlp_select"] = (2 * T * (2 * R * R + (E + 1) * R), T * R * A + 2 * R * R * A + T * (E + 1) * A
                                 + (T - n_routed) * H * 4 * 2)
     out["buckets"] = (0, T * 4 + n_routed * 4)
-    out["expert_gate_up"] = (2 * n_routed * H * 2 * I, n_used * 2 * I * H * A + n_routed * H * A + n_routed * I * A)
-    out["expert_down_merge"] = (2 * n_routed * I * H, n_used * H * I * A + n_routed * I * A + n_routed * H * 4 * 2)
+    # expert weights: act bytes, or one E4M3 byte per weight plus an fp32 scale per row
+    fp8 = getattr(cfg, "expert_format", "act") == "fp8"
+    wgu = n_used * (2 * I * H + 2 * I * 4) if fp8 else n_used * 2 * I * H * A
+    wdn = n_used * (H * I + H * 4) if fp8 else n_used * H * I * A
+    out["expert_gate_up"] = (2 * n_routed * H * 2 * I, wgu + n_routed * H * A + n_routed * I * A)
+    out["expert_down_merge"] = (2 * n_routed * I * H, wdn + n_routed * I * A + n_routed * H * 4 * 2)
     return out
 
 
@@ -367,6 +371,10 @@ def main():
         dec = measure(dcfg, args.steps, args.warmup, hip)
         print(f"[bench] decode {dec['ms']:.4f} ms/step, {dec['graph_ms']:.4f} ms/step as a graph replay",
               file=sys.stderr, flush=True)
+    dec8 = None
+    if not args.no_decode:
+        dec8 = measure(CONFIGS["decode_fp8"], args.steps, args.warmup, hip)
+        print(f"[bench] decode with FP8 experts {dec8['ms']:.4f} ms/step", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(pcfg)
     T = pcfg.tokens
     value = T / (pre["ms"] * 1e-3)
@@ -393,6 +401,13 @@ def main():
                           "experts_used": dec["experts_used"], "roofline": dec["roofline"], "stages": dec["stages"],
                           "graph": {"ms_per_step": round(dec["graph_ms"], 5),
                                     "tok_s": round(dcfg.batch / (dec["graph_ms"] * 1e-3), 1)}}
+    if dec8 is not None:
+        dcfg = CONFIGS["decode_fp8"]
+        line["decode_fp8_experts"] = {
+            "tok_s": round(dcfg.batch / (dec8["ms"] * 1e-3), 1), "ms_per_step": round(dec8["ms"], 5),
+            "step_mbytes": round(dec8["step_mbytes"], 1),
+            "frac_of_hbm_peak": round(dec8["step_mbytes"] / (dec8["ms"] * 1e-3) / 1e3 / PEAK_HBM_GBS, 4),
+            "experts_used": dec8["experts_used"], "roofline": dec8["roofline"], "stages": dec8["stages"]}
     print(json.dumps(line))
 
 

@@ -39,15 +39,23 @@
 extern "C" {
 #endif
 
-#define ZAYA_ABI_VERSION 1
+#define ZAYA_ABI_VERSION 2
 
 enum zaya_dtype { ZAYA_F32 = 0, ZAYA_BF16 = 1 };
+
+/* Storage of the expert weights W_gu and W_dn. ZAYA_EXPERTS_ACT: the act dtype, like
+ * every other weight. ZAYA_EXPERTS_FP8_E4M3: one byte per weight in the OCP FP8 E4M3
+ * format (sign, 4 exponent bits with bias 7, 3 mantissa bits; finite values only), with
+ * one fp32 scale per weight row: the weight is code_value * scale. A low-precision
+ * deployment of the experts, like the quantized ZAYA1 bundles (the JANGTQ2 card's
+ * "Quantization" section); it needs act_dtype ZAYA_BF16. */
+enum zaya_expert_format { ZAYA_EXPERTS_ACT = 0, ZAYA_EXPERTS_FP8_E4M3 = 1 };
 
 enum zaya_status {
   ZAYA_OK = 0,
   ZAYA_EINVAL = -1,     /* a required pointer is NULL, or B/S <= 0 */
   ZAYA_ESHAPE = -2,     /* configuration outside what the kernels support */
-  ZAYA_EDTYPE = -3,     /* unknown act dtype */
+  ZAYA_EDTYPE = -3,     /* unknown act dtype or expert format, or an unsupported pairing */
   ZAYA_EWORKSPACE = -4, /* workspace NULL or smaller than the *_workspace_bytes query */
   ZAYA_ECACHE = -5,     /* cache_len[b] < 0 or cache_len[b] + S > cap */
   ZAYA_EALIAS = -6,     /* an output aliases an input it must not alias */
@@ -72,6 +80,7 @@ typedef struct zaya_block_config {
   int sliding_window;  /* < 0: off; else key k visible from query q iff 0 <= p_q - p_k <= window */
   float rms_eps;       /* rms_norm_eps */
   int act_dtype;       /* enum zaya_dtype */
+  int expert_format;   /* enum zaya_expert_format (0: the act dtype) */
 } zaya_block_config;
 
 /* Device pointers to one block's parameters, act dtype unless noted.
@@ -85,7 +94,10 @@ typedef struct zaya_block_config {
  * r_Wd [R, H], r_bd [R], r_rss [R] (router_states_scale), r_norm_g [R], r_W1, r_W2
  *   [R, R], r_b1, r_b2 [R], r_Wout [E+1, R].
  * bal_bias: fp32 [E+1] (balancing_biases). W_gu [E, 2I, H]: gate rows then up rows.
- * W_dn [E, H, I]. */
+ * W_dn [E, H, I]. With expert_format ZAYA_EXPERTS_FP8_E4M3, W_gu and W_dn hold E4M3
+ * bytes in the same layouts and W_gu_scale fp32 [E, 2I], W_dn_scale fp32 [E, H] their
+ * row scales (both required); with ZAYA_EXPERTS_ACT the two scale pointers are
+ * ignored. */
 typedef struct zaya_block_weights {
   const void* ln1_g;
   const void* W_qkv;
@@ -114,6 +126,8 @@ typedef struct zaya_block_weights {
   const void* m_hss;
   const void* m_rb;
   const void* m_rs;
+  const float* W_gu_scale;
+  const float* W_dn_scale;
 } zaya_block_weights;
 
 /* Per-block decode state (JANGTQ2 card, "Architecture Summary"): the KV cache plus

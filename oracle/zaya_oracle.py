@@ -369,6 +369,30 @@ def buckets(cls_flat, num_experts):
     return offsets, np.concatenate(ids).astype(np.int64)
 
 
+def e4m3_value(code):
+    """Value of an OCP FP8 E4M3 byte, from the format's definition: bit 7 sign, bits
+    6..3 exponent with bias 7, bits 2..0 mantissa; exponent 0 is subnormal
+    (mantissa/8 * 2^-6); the all-ones pattern S.1111.111 is NaN (the format has no
+    infinities). Exact in float64."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = (c & 0x7).astype(np.float64)
+    normal = (1.0 + man / 8.0) * np.exp2(ex.astype(np.float64) - 7.0)
+    sub = man / 8.0 * 2.0 ** -6
+    v = sign * np.where(ex == 0, sub, normal)
+    return np.where((ex == 15) & ((c & 7) == 7), np.nan, v)
+
+
+def expert_weight(cfg, w, name, e):
+    """Weight matrix of expert e in float64: the stored act values, or with FP8 storage
+    the E4M3 byte values times their row scales (fp32)."""
+    if getattr(cfg, "expert_format", "act") == "fp8":
+        q = np.asarray(w[name][e])
+        return e4m3_value(q) * f64(np.asarray(w[name + "_scale"][e]))[:, None]
+    return w[name][e]
+
+
 def expert(cfg, w, e, x, rnd):
     """SwiGLU expert e on rows x: down(rnd(silu(gate x)) * up x).
 
@@ -377,12 +401,12 @@ def expert(cfg, w, e, x, rnd):
     Returns (activation, neurons, y).
     """
     I = cfg.moe_intermediate_size
-    Wgu = w["W_gu"][e]
+    Wgu = expert_weight(cfg, w, "W_gu", e)
     G = linear(x, Wgu[:I], rnd)
     U = linear(x, Wgu[I:], rnd)
     act = rnd(silu(G))
     nrn = rnd(act * U)
-    y = linear(nrn, w["W_dn"][e], rnd)
+    y = linear(nrn, expert_weight(cfg, w, "W_dn", e), rnd)
     return act, nrn, y
 
 

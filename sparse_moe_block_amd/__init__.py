@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzaya.so")
 
 ZAYA_F32, ZAYA_BF16 = 0, 1
+ZAYA_EXPERTS_ACT, ZAYA_EXPERTS_FP8_E4M3 = 0, 1
 STATUS = {0: "ZAYA_OK", -1: "ZAYA_EINVAL", -2: "ZAYA_ESHAPE", -3: "ZAYA_EDTYPE", -4: "ZAYA_EWORKSPACE",
           -5: "ZAYA_ECACHE", -6: "ZAYA_EALIAS", -7: "ZAYA_EHIP"}
 
@@ -36,12 +37,12 @@ class BlockConfig(C.Structure):
     _fields_ = [("hidden", C.c_int), ("n_heads", C.c_int), ("n_kv_heads", C.c_int), ("head_dim", C.c_int),
                 ("rope_dim", C.c_int), ("rope_theta", C.c_float), ("conv_k", C.c_int), ("n_experts", C.c_int),
                 ("expert_inter", C.c_int), ("router_hidden", C.c_int), ("sliding_window", C.c_int),
-                ("rms_eps", C.c_float), ("act_dtype", C.c_int)]
+                ("rms_eps", C.c_float), ("act_dtype", C.c_int), ("expert_format", C.c_int)]
 
 
 WEIGHT_FIELDS = ("ln1_g", "W_qkv", "conv_w", "conv_b", "temp", "W_o", "a_hsb", "a_hss", "a_rb", "a_rs", "ln2_g",
                  "r_Wd", "r_bd", "r_rss", "r_norm_g", "r_W1", "r_b1", "r_W2", "r_b2", "r_Wout", "bal_bias", "W_gu",
-                 "W_dn", "m_hsb", "m_hss", "m_rb", "m_rs")
+                 "W_dn", "m_hsb", "m_hss", "m_rb", "m_rs", "W_gu_scale", "W_dn_scale")
 
 
 class BlockWeights(C.Structure):
@@ -123,11 +124,13 @@ def block_config(cfg) -> BlockConfig:
                        float(cfg.rope_theta), getattr(cfg, "conv_k", 3), cfg.num_experts,
                        cfg.moe_intermediate_size, cfg.router_hidden, getattr(cfg, "sliding_window", -1),
                        float(getattr(cfg, "rms_norm_eps", 1e-5)),
-                       ZAYA_BF16 if cfg.act_dtype == "bf16" else ZAYA_F32)
+                       ZAYA_BF16 if cfg.act_dtype == "bf16" else ZAYA_F32,
+                       ZAYA_EXPERTS_FP8_E4M3 if getattr(cfg, "expert_format", "act") == "fp8" else ZAYA_EXPERTS_ACT)
 
 
 def block_weights(w: Mapping) -> BlockWeights:
-    return BlockWeights(*[_ptr(w[n]) for n in WEIGHT_FIELDS])
+    """Weights by field name; the two expert scale tensors are optional (fp8 experts)."""
+    return BlockWeights(*[_ptr(w.get(n)) for n in WEIGHT_FIELDS])
 
 
 def cca_cache(cache: Optional[Mapping]):

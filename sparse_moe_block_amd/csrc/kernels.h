@@ -123,9 +123,14 @@ struct MoeArgs {
   T* routed_tap;  // or NULL
   T* mlp_tap;     // or NULL
   int ntok, H, I, E;
+  const float* gu_scale = nullptr;  // FP8 experts: row scales [E, 2I] and [E, H]
+  const float* dn_scale = nullptr;
 };
 template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s);
+// FP8 (E4M3) expert weights with fp32 row scales, bf16 activations
+hipError_t launch_moe_gateup_f8(const MoeArgs<bf16_t>& a, hipStream_t s);
+hipError_t launch_moe_down_f8(const MoeArgs<bf16_t>& a, hipStream_t s);
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s);
 

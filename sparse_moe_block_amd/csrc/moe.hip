@@ -257,6 +257,171 @@ hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
   return launch_down_cfg<T, 64, 2, 2>(a, s);
 }
 
+// ----------------------------------------------------------------------------- FP8 experts
+//
+// Expert weights stored as OCP FP8 E4M3 bytes with one fp32 scale per weight row
+// (weight = byte value x scale); activations bf16. A workgroup takes one item =
+// (expert, tile of up to 16 of its tokens, 64 output rows): the token rows are staged
+// once in LDS (whole K, rows padded by 16 bytes so the fragment reads of 16 rows hit
+// distinct banks), and each wave streams its 16 weight rows (gate/up: 16 gate and the
+// matching 16 up rows) straight from memory into registers, 16 bytes per lane per 64
+// K elements, eight such loads ahead of the MFMAs. The bytes are widened to bf16 in
+// registers (exactly: every E4M3 value is a bf16 value) and fed to the bf16 MFMA; the
+// row scale multiplies the fp32 sum before the rounding the bf16 path applies. K is
+// visited in a fixed order per lane group (elements 64 s + 16 grp .. + 16 for both
+// operands), which only permutes the terms of each dot product.
+constexpr int kF8Tok = 16;
+constexpr int kF8Ahead = 8;
+
+__device__ __forceinline__ void f8x16_to_bf16(const u32x4 q, bf16x8_t& lo, bf16x8_t& hi) {
+  u32x4 a, b;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[k], false);
+    const f32x2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[k], true);
+    a[2 * k] = pack_bf16x2(p0.x, p0.y);
+    a[2 * k + 1] = pack_bf16x2(p1.x, p1.y);
+    const f32x2_t r0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[k + 2], false);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[k + 2], true);
+    b[2 * k] = pack_bf16x2(r0.x, r0.y);
+    b[2 * k + 1] = pack_bf16x2(r1.x, r1.y);
+  }
+  lo = __builtin_bit_cast(bf16x8_t, a);
+  hi = __builtin_bit_cast(bf16x8_t, b);
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void moe_f8_kernel(MoeArgs<bf16_t> a) {
+  extern __shared__ __attribute__((aligned(16))) char xs[];  // kF8Tok rows x (K bf16 + 16 bytes)
+  const int K = GATEUP ? a.H : a.I;
+  const int ntn = (GATEUP ? a.I : a.H) / 64;
+  int e, r0, n_e, j;
+  if (!moe_item(a.offsets, a.E, kF8Tok, ntn, e, r0, n_e, j)) return;
+  const int base = a.offsets[e] + r0;
+  const int rows = min(kF8Tok, n_e - r0);
+  const int pitch = K * 2 + 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+
+  // weight rows of this lane (byte pointers at its 16-byte column) and the first loads
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(GATEUP ? (const void*)a.W_gu : (const void*)a.W_dn) +
+                     (size_t)e * (GATEUP ? 2 * (size_t)a.I * a.H : (size_t)a.H * a.I);
+  const int n_row = 64 * j + 16 * wave + r16;  // gate row (gate/up) or output row (down)
+  const uint8_t* w0 = W + (size_t)n_row * K + grp * 16;
+  const uint8_t* w1 = W + (size_t)(GATEUP ? a.I + n_row : n_row) * K + grp * 16;
+  const int nds = K / 64;
+  u32x4 q0[kF8Ahead], q1[kF8Ahead];
+#pragma unroll
+  for (int p = 0; p < kF8Ahead; ++p) {
+    const int s = min(p, nds - 1);
+    q0[p] = *reinterpret_cast<const u32x4*>(w0 + (size_t)s * 64);
+    if (GATEUP) q1[p] = *reinterpret_cast<const u32x4*>(w1 + (size_t)s * 64);
+  }
+
+  // stage the token rows (rows past the tile repeat its last row; never stored)
+  {
+    const int cpr = K / 8;  // 16-byte chunks per row
+    for (int c0 = threadIdx.x; c0 < kF8Tok * cpr; c0 += 256 * 4) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch = c0 + u * 256;
+        if (ch < kF8Tok * cpr) {
+          const int r = ch / cpr, cc = ch % cpr;
+          const int rr = min(r, rows - 1);
+          const bf16_t* src = GATEUP ? a.hn + (size_t)a.ids[base + rr] * a.H : a.neurons + (size_t)(base + rr) * a.I;
+          v[u] = *reinterpret_cast<const u32x4*>(src + cc * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch = c0 + u * 256;
+        if (ch < kF8Tok * cpr) *reinterpret_cast<u32x4*>(xs + (ch / cpr) * pitch + (ch % cpr) * 16) = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  const char* xrow = xs + r16 * pitch + grp * 32;
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int s0 = 0; s0 < nds; s0 += kF8Ahead) {
+#pragma unroll
+    for (int p = 0; p < kF8Ahead; ++p) {
+      const int s = s0 + p;
+      if (s < nds) {
+        const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(xrow + (size_t)s * 128));
+        const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(xrow + (size_t)s * 128 + 16));
+        bf16x8_t wa, wb;
+        f8x16_to_bf16(q0[p], wa, wb);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc0, 0, 0, 0);
+        if (GATEUP) {
+          f8x16_to_bf16(q1[p], wa, wb);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc1, 0, 0, 0);
+        }
+        // refill this slot kF8Ahead steps ahead (past the end: the last step again)
+        const int sn = min(s + kF8Ahead, nds - 1);
+        q0[p] = *reinterpret_cast<const u32x4*>(w0 + (size_t)sn * 64);
+        if (GATEUP) q1[p] = *reinterpret_cast<const u32x4*>(w1 + (size_t)sn * 64);
+      }
+    }
+  }
+
+  // lane holds rows n = 16 wave + 4 grp + i of the item's 64, for token r16
+  if (r16 >= rows) return;
+  const int n0 = 64 * j + 16 * wave + 4 * grp;
+  if (GATEUP) {
+    float sg[4], su[4], v[4];
+    load4(a.gu_scale + (size_t)e * 2 * a.I + n0, sg);
+    load4(a.gu_scale + (size_t)e * 2 * a.I + a.I + n0, su);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gt = Act<bf16_t>::rnd(acc0[i] * sg[i]);
+      const float ut = Act<bf16_t>::rnd(acc1[i] * su[i]);
+      const float act = Act<bf16_t>::rnd(gt / (1.0f + expf(-gt)));
+      v[i] = Act<bf16_t>::rnd(act * ut);
+    }
+    store4(a.neurons + (size_t)(base + r16) * a.I + n0, v);
+  } else {
+    const int tok = a.ids[base + r16];
+    const float wt = Act<bf16_t>::tof(a.wts[tok]);
+    float sd[4], hv[4], b1[4], s1[4], b2[4], s2[4], ro[4], mo[4], o[4];
+    load4(a.dn_scale + (size_t)e * a.H + n0, sd);
+    load4(a.h + (size_t)tok * a.H + n0, hv);
+    load4(a.hsb + n0, b1);
+    load4(a.hss + n0, s1);
+    load4(a.rb + n0, b2);
+    load4(a.rs + n0, s2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = Act<bf16_t>::rnd(acc0[i] * sd[i]);
+      ro[i] = Act<bf16_t>::rnd(wt * y);
+      mo[i] = Act<bf16_t>::rnd(Act<bf16_t>::rnd(ro[i] + b1[i]) * s1[i]);
+      o[i] = fadd(fmul(fadd(hv[i], b2[i]), s2[i]), mo[i]);
+    }
+    store4(a.out + (size_t)tok * a.H + n0, o);
+    if (a.routed_tap) store4(a.routed_tap + (size_t)tok * a.H + n0, ro);
+    if (a.mlp_tap) store4(a.mlp_tap + (size_t)tok * a.H + n0, mo);
+  }
+}
+
+template <bool GATEUP>
+static hipError_t launch_f8(const MoeArgs<bf16_t>& a, hipStream_t s) {
+  if (a.ntok <= 0) return hipSuccess;
+  const int K = GATEUP ? a.H : a.I;
+  const size_t lds = (size_t)kF8Tok * (K * 2 + 16);
+  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_f8_kernel<GATEUP>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(moe_f8_kernel<GATEUP>, dim3(moe_grid(a.ntok, a.E, kF8Tok, (GATEUP ? a.I : a.H) / 64)),
+                     dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gateup_f8(const MoeArgs<bf16_t>& a, hipStream_t s) { return launch_f8<true>(a, s); }
+hipError_t launch_moe_down_f8(const MoeArgs<bf16_t>& a, hipStream_t s) { return launch_f8<false>(a, s); }
+
 template hipError_t launch_moe_gateup<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);
 template hipError_t launch_moe_gateup<float>(const MoeArgs<float>&, hipStream_t);
 template hipError_t launch_moe_down<bf16_t>(const MoeArgs<bf16_t>&, hipStream_t);

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -56,6 +57,12 @@ int check_config(const zaya_block_config* c) {
   if (c->router_hidden != 256) return fail(ZAYA_ESHAPE, "router_hidden %d != 256", c->router_hidden);
   if (!(c->rms_eps > 0.f)) return fail(ZAYA_ESHAPE, "rms_eps must be > 0");
   if (!(c->rope_theta > 0.f)) return fail(ZAYA_ESHAPE, "rope_theta must be > 0");
+  if (c->expert_format != ZAYA_EXPERTS_ACT && c->expert_format != ZAYA_EXPERTS_FP8_E4M3)
+    return fail(ZAYA_EDTYPE, "expert_format %d", c->expert_format);
+  if (c->expert_format == ZAYA_EXPERTS_FP8_E4M3) {
+    if (c->act_dtype != ZAYA_BF16) return fail(ZAYA_EDTYPE, "FP8 experts need act_dtype ZAYA_BF16");
+    if (c->expert_inter > 4096) return fail(ZAYA_ESHAPE, "FP8 experts: expert_inter %d > 4096", c->expert_inter);
+  }
   return ZAYA_OK;
 }
 
@@ -123,8 +130,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
-int check_weights(const zaya_block_weights* w) {
+int check_weights(const zaya_block_config* c, const zaya_block_weights* w) {
   if (!w) return fail(ZAYA_EINVAL, "weights is NULL");
+  if (c->expert_format == ZAYA_EXPERTS_FP8_E4M3 && (!w->W_gu_scale || !w->W_dn_scale))
+    return fail(ZAYA_EINVAL, "FP8 experts need W_gu_scale and W_dn_scale");
   const void* ptrs[] = {w->ln1_g, w->W_qkv, w->conv_w, w->conv_b, w->temp, w->W_o, w->a_hsb, w->a_hss, w->a_rb,
                         w->a_rs, w->ln2_g, w->r_Wd, w->r_bd, w->r_rss, w->r_norm_g, w->r_W1, w->r_b1, w->r_W2,
                         w->r_b2, w->r_Wout, w->bal_bias, w->W_gu, w->W_dn, w->m_hsb, w->m_hss, w->m_rb, w->m_rs};
@@ -254,10 +263,21 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   // a10/a11: experts, weighted combine, MoE merge
   MoeArgs<T> ma{offsets, ids, hn, W(w->W_gu), W(w->W_dn), neurons, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb),
                 W(w->m_rs), x_out, (T*)tp.routed_output, (T*)tp.mlp_output, T_, H, I, E};
+  ma.gu_scale = w->W_gu_scale;
+  ma.dn_scale = w->W_dn_scale;
+  const bool f8 = c->expert_format == ZAYA_EXPERTS_FP8_E4M3;  // act is bf16 (checked)
   HIPCHK(mark(9));
-  HIPCHK(launch_moe_gateup<T>(ma, st));
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    HIPCHK(f8 ? launch_moe_gateup_f8(ma, st) : launch_moe_gateup<T>(ma, st));
+  } else {
+    HIPCHK(launch_moe_gateup<T>(ma, st));
+  }
   HIPCHK(mark(10));
-  HIPCHK(launch_moe_down<T>(ma, st));
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    HIPCHK(f8 ? launch_moe_down_f8(ma, st) : launch_moe_down<T>(ma, st));
+  } else {
+    HIPCHK(launch_moe_down<T>(ma, st));
+  }
   HIPCHK(mark(11));
   HIPCHK(tap_copy(tp.mlp_neurons, neurons, (size_t)T_ * I * A));
   HIPCHK(tap_copy(tp.layer_output, x_out, (size_t)T_ * H * 4));
@@ -273,7 +293,7 @@ int block_entry(const zaya_block_config* c, const zaya_block_weights* w, int B, 
   g_err.clear();
   int rc = check_config(c);
   if (rc) return rc;
-  if ((rc = check_weights(w))) return rc;
+  if ((rc = check_weights(c, w))) return rc;
   if (B <= 0 || S <= 0) return fail(ZAYA_EINVAL, "B=%d S=%d must be positive", B, S);
   if (decode && S != 1) return fail(ZAYA_EINVAL, "decode needs S == 1");
   if (!x || !x_out || !s_out) return fail(ZAYA_EINVAL, "x, x_out and router_state_out are required");
@@ -370,7 +390,7 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
   if (!w || !w->embed || !w->emb_shift || !w->emb_scale || !w->final_g || !w->blocks)
     return fail(ZAYA_EINVAL, "stack weights incomplete");
   for (int l = 0; l < cfg->n_layers; ++l)
-    if ((rc = check_weights(&w->blocks[l]))) return fail(rc, "block %d: %s", l, g_err.c_str());
+    if ((rc = check_weights(&cfg->block, &w->blocks[l]))) return fail(rc, "block %d: %s", l, g_err.c_str());
   if (B <= 0 || S <= 0) return fail(ZAYA_EINVAL, "B=%d S=%d must be positive", B, S);
   if (!ids || !logits) return fail(ZAYA_EINVAL, "ids and logits are required");
   if (caches) {

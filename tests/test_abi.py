@@ -116,7 +116,7 @@ def test_argument_errors_have_their_codes(L):
     cases = [
         (dict(cfg=None), -1),
         (dict(w=None), -1),
-        (dict(w=C.byref(Z.BlockWeights(*([FAKE] * (len(Z.WEIGHT_FIELDS) - 1) + [None])))), -1),
+        (dict(w=C.byref(Z.BlockWeights(*([FAKE] * 26 + [None] + [FAKE] * (len(Z.WEIGHT_FIELDS) - 27))))), -1),
         (dict(B=0), -1),
         (dict(S=-3), -1),
         (dict(x=None), -1),
@@ -143,6 +143,27 @@ def test_bad_dtype(L):
     bc.act_dtype = 7
     rc = _prefill(L, _args(cfg, 1, 8, cfg=C.byref(bc), ws_bytes=0))
     assert rc == -3
+    bc = Z.block_config(cfg)
+    bc.expert_format = 5
+    assert _prefill(L, _args(cfg, 1, 8, cfg=C.byref(bc), ws_bytes=0)) == -3
+
+
+def test_fp8_experts_validation(L):
+    # FP8 experts need bf16 activations and both row-scale tensors
+    f32 = CONFIGS["tiny"].replace(expert_format="fp8")
+    assert _prefill(L, _args(f32, 1, 8, ws_bytes=0)) == -3
+    assert "BF16" in L.zaya_last_error().decode()
+    cfg = CONFIGS["decode_fp8"]
+    fields = [FAKE] * len(Z.WEIGHT_FIELDS)
+    fields[Z.WEIGHT_FIELDS.index("W_dn_scale")] = None
+    rc = _prefill(L, _args(cfg, 1, 8, w=C.byref(Z.BlockWeights(*fields)), ws_bytes=0))
+    assert rc == -1 and "scale" in L.zaya_last_error().decode()
+    # with the scales present, validation reaches the workspace check
+    assert _prefill(L, _args(cfg, 1, 8, ws_bytes=0)) == -4
+    # act-format experts ignore the scale pointers
+    fields = [FAKE] * len(Z.WEIGHT_FIELDS)
+    fields[-1] = fields[-2] = None
+    assert _prefill(L, _args(CONFIGS["prefill"], 1, 8, w=C.byref(Z.BlockWeights(*fields)), ws_bytes=0)) == -4
 
 
 def test_cache_bounds_are_checked(L):

@@ -115,3 +115,16 @@ def test_long_context_window_zipf_sampled_rows():
     print("long context expert counts:", counts.tolist(), "skip:", T - int(offs[-1]), flush=True)
     # the load is strongly skewed: the first expert carries several times the last one's tokens
     assert counts[0] > 5 * counts[-1] and (T - offs[-1]) > 0.1 * T
+
+
+def test_fp8_experts_decode_workload():
+    """The decode workload with the expert weights stored as FP8 E4M3 bytes and fp32 row
+    scales: every row and tap against the oracle on the decoded weights."""
+    _full_check(CONFIGS["decode_fp8"])
+
+
+def test_fp8_experts_prefill_several_token_tiles():
+    """FP8 experts on a short prefill, where experts receive more than one 16-token tile."""
+    run, ref, r = _full_check(small_bf16(name="small_fp8", expert_format="fp8", batch=2, seq=160))
+    counts = np.diff(run.taps["bucket_offsets"].cpu().numpy())
+    assert counts.max() > 16

@@ -57,6 +57,7 @@ class ZayaConfig:
     conv_std: float = 0.02  # std of the conv taps and bias
     gain_std: float = 0.0  # RMSNorm gains: 1 + N(0, gain_std); 0 = ones
     bal_bias: str = "zeros"  # "zeros", "normal", "trained", "zipf"
+    expert_format: str = "act"  # "act" or "fp8": expert weights stored as E4M3 bytes + fp32 row scales
 
     @property
     def conv_channels(self) -> int:
@@ -99,6 +100,9 @@ CONFIGS: Dict[str, ZayaConfig] = {
     "prefill": ZayaConfig(name="prefill", **_full(batch=1, seq=4096)),
     # block decode, bf16, B64, 8192 cached tokens, one new token each
     "decode": ZayaConfig(name="decode", **_full(batch=64, seq=1, kv_len=8192, decode=True)),
+    # the same decode step with the expert weights stored as FP8 E4M3 + fp32 row scales
+    "decode_fp8": ZayaConfig(name="decode_fp8", **_full(batch=64, seq=1, kv_len=8192, decode=True,
+                                                        expert_format="fp8")),
     # 40-block stack prefill, bf16, B4 S2048, vocab 262144
     "stack": ZayaConfig(name="stack", **_full(batch=4, seq=2048, num_layers=40, vocab_size=262144)),
     # long-context prefill, bf16, B1 S32768, window 4096, Zipf(1.2) expert load + 15% skip
@@ -229,7 +233,24 @@ def block_weights(cfg: ZayaConfig, block: int = 0, seed: int = 0,
         bb = np.zeros(E + 1, np.float32)
     # the buffer holds bf16-representable values
     w["bal_bias"] = torch.from_numpy(bb).to(torch.bfloat16).float()
+    if cfg.expert_format == "fp8":
+        w.update(fp8_rows(w.pop("W_gu"), "W_gu"))
+        w.update(fp8_rows(w.pop("W_dn"), "W_dn"))
     return w
+
+
+def fp8_rows(W: torch.Tensor, name: str) -> Dict[str, torch.Tensor]:
+    """Storage of a weight tensor as OCP FP8 E4M3 bytes with one fp32 scale per row
+    (last dimension = row): scale = max|row| / 448 (448 is the largest E4M3 value), the
+    bytes are torch's round-to-nearest conversion of row / scale. Returns
+    {name: uint8 tensor of W's shape, name + "_scale": fp32 tensor of W.shape[:-1]}.
+    This is how the synthetic weights are stored; the dequantization (byte value times
+    scale) is the block's arithmetic and is not done here."""
+    Wf = W.float()
+    amax = Wf.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (Wf / scale.unsqueeze(-1)).to(torch.float8_e4m3fn)
+    return {name: q.view(torch.uint8).contiguous(), name + "_scale": scale.contiguous()}
 
 
 def _device_stream(seed: int, cfg_name: str, block: int, tensor: str, device) -> torch.Generator:
