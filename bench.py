@@ -152,7 +152,10 @@ def stage_work(cfg, n_routed: int, n_used: int):
     out["qkv_proj"] = (2 * T * H * QR + (2 * B * H * nkv * d // 2 if L0 else 0),
                        T * H * A + QR * H * A + T * QR * A + (B * H * A if L0 else 0))
     # conv_state read + written, prev_hs written
-    out["cca"] = (0, T * QR * A + T * nh * d * A + 2 * T * nkv * d * A + C * 4 * A + B * (C * 2 * 2 + H) * A)
+    # taps and biases: kernel 3 + bias, or depthwise k2 + bias and grouped k2 (2 d per channel) + bias
+    conv_w = C * 4 * A if cfg.conv_k == 3 else C * (3 + 2 * d + 1) * A
+    out["cca"] = (2 * T * C * 2 * d if cfg.conv_k == 2 else 0,
+                  T * QR * A + T * nh * d * A + 2 * T * nkv * d * A + conv_w + B * (C * 2 * 2 + H) * A)
     out["attention"] = (4 * d * nh * pairs, T * nh * d * A * 2 + kv_read)
     out["o_proj_merge"] = (2 * T * nh * d * H, T * nh * d * A + H * nh * d * A + T * H * 4 * 2 + 4 * H * A)
     out["post_attn_norm"] = (0, T * H * 4 + T * H * A + H * A)
@@ -341,7 +344,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="time only the headline prefill workload")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (a kernel of known traffic for "
@@ -375,6 +378,10 @@ def main():
     if not args.no_decode:
         dec8 = measure(CONFIGS["decode_fp8"], args.steps, args.warmup, hip)
         print(f"[bench] decode with FP8 experts {dec8['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    pre2 = None
+    if not args.no_decode:
+        pre2 = measure(CONFIGS["prefill_conv2"], args.steps, args.warmup, hip)
+        print(f"[bench] prefill with the two-stage conv {pre2['ms']:.4f} ms/step", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(pcfg)
     T = pcfg.tokens
     value = T / (pre["ms"] * 1e-3)
@@ -408,6 +415,10 @@ def main():
             "step_mbytes": round(dec8["step_mbytes"], 1),
             "frac_of_hbm_peak": round(dec8["step_mbytes"] / (dec8["ms"] * 1e-3) / 1e3 / PEAK_HBM_GBS, 4),
             "experts_used": dec8["experts_used"], "roofline": dec8["roofline"], "stages": dec8["stages"]}
+    if pre2 is not None:
+        c2 = CONFIGS["prefill_conv2"]
+        line["prefill_two_stage_conv"] = {"tok_s": round(c2.tokens / (pre2["ms"] * 1e-3), 1),
+                                          "ms_per_step": round(pre2["ms"], 5), "cca": pre2["stages"]["cca"]}
     print(json.dumps(line))
 
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ZAYA_ABI_VERSION 2
+#define ZAYA_ABI_VERSION 3
 
 enum zaya_dtype { ZAYA_F32 = 0, ZAYA_BF16 = 1 };
 
@@ -64,8 +64,9 @@ enum zaya_status {
 
 /* Block shape ("Config" and "Printout" on the nnterp page). Supported: head_dim in
  * {64, 128}; n_heads % n_kv_heads == 0 with n_heads / n_kv_heads in {1, 2, 4, 8};
- * rope_dim even and <= head_dim; conv_k == 3; n_experts + 1 <= 32; hidden a multiple
- * of 256 and <= 4096; expert_inter a multiple of 64; router_hidden == 256. */
+ * rope_dim even and <= head_dim; conv_k 3 or 2 (with conv_k 2 in fp32, head_dim 64 or
+ * n_heads / n_kv_heads <= 4); n_experts + 1 <= 32; hidden a multiple of 256 and <= 4096;
+ * expert_inter a multiple of 64; router_hidden == 256. */
 typedef struct zaya_block_config {
   int hidden;          /* H (hidden_size) */
   int n_heads;         /* query heads (num_attention_heads) */
@@ -73,7 +74,8 @@ typedef struct zaya_block_config {
   int head_dim;        /* d */
   int rope_dim;        /* rotated leading dims of each head (partial_rotary_factor * d) */
   float rope_theta;    /* rotary base */
-  int conv_k;          /* causal conv kernel over the q/k channels; must be 3 */
+  int conv_k;          /* q/k convolution: 3 = one depthwise kernel-3 conv; 2 = depthwise
+                          kernel 2 then grouped kernel 2, one group per head ("Printout") */
   int n_experts;       /* E routed experts; the router scores E + 1 classes (last = skip) */
   int expert_inter;    /* I (moe_intermediate_size) */
   int router_hidden;   /* R (router down_proj width) */
@@ -87,7 +89,11 @@ typedef struct zaya_block_config {
  * W_qkv [n_heads*d + n_kv_heads*d + 2*(n_kv_heads*d/2), H]: rows q_proj, k_proj,
  *   v_proj_current, v_proj_delayed ("Printout": ZayaCCAProjection).
  * conv_w [C, 3], conv_b [C], C = (n_heads + n_kv_heads) * d: the q channels (head-major)
- *   then the k channels; tap 2 multiplies the current token.
+ *   then the k channels; tap 2 multiplies the current token. With conv_k == 2, conv_w
+ *   is [C, 2] (conv_qk_depthwise: tap 0 the previous token, tap 1 the current) and
+ *   conv2_w [C, 2, d], conv2_b [C] are conv_qk_grouped: output channel, tap (0 previous,
+ *   1 current), input channel within the output channel's head; both are required then
+ *   and ignored with conv_k == 3.
  * temp [n_kv_heads]: key temperature. W_o [H, n_heads*d].
  * a_* / m_* [H]: hidden_states_bias (hsb), hidden_states_scale (hss), residual_bias
  *   (rb), residual_scale (rs) of the attention and MoE merges.
@@ -128,12 +134,16 @@ typedef struct zaya_block_weights {
   const void* m_rs;
   const float* W_gu_scale;
   const float* W_dn_scale;
+  const void* conv2_w;
+  const void* conv2_b;
 } zaya_block_weights;
 
 /* Per-block decode state (JANGTQ2 card, "Architecture Summary"): the KV cache plus
  * conv_state and prev_hs. K, V [B, n_kv_heads, cap, d]; new tokens are written at
- * positions cache_len[b] .. cache_len[b]+S-1. conv_state [B, C, 2]: slot 0 = the
- * q/k conv input two tokens back, slot 1 = one token back. prev_hs [B, H]: the
+ * positions cache_len[b] .. cache_len[b]+S-1. conv_state [B, C, 2]: with conv_k == 3
+ * slot 0 = the q/k conv input two tokens back, slot 1 = one token back; with conv_k
+ * == 2 slot 0 = the input one token back, slot 1 = the depthwise conv's output one
+ * token back. prev_hs [B, H]: the
  * previous token's normed input (attention_norm_output). A sequence with
  * cache_len[b] == 0 is fresh: its history reads as zeros whatever the buffers hold.
  * conv_state and prev_hs are updated in place; cache_len is never written (the

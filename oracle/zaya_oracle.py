@@ -184,6 +184,35 @@ def causal_conv3(cin, hist, cw, cb):
     return y, ext
 
 
+def causal_conv_two_stage(cin, x_prev, y1_prev, w1, b1, w2, b2, groups, rnd):
+    """The printout's two causal convolutions over the q/k channels, one sequence.
+
+    ("Printout": conv_qk_depthwise = Conv1d(C, C, kernel 2, groups C) and
+    conv_qk_grouped = Conv1d(C, C, kernel 2, groups 10), both with bias; "Queries and
+    keys are convolved ...": together they mix the current and two previous tokens.)
+      y1_t = rnd(b1 + w1[:,0] x_{t-1} + w1[:,1] x_t)                  (depthwise)
+      y2_t = rnd(b2 + W2[:,0,:] y1_{t-1} + W2[:,1,:] y1_t)  per group   (grouped)
+    cin: [S, C]; x_prev, y1_prev: [C] the input and the depthwise output one token
+    before the call (zeros for a fresh sequence); w1 [C, 2], b1 [C]; w2 [C, 2, C/groups]
+    (output channel, tap, input channel of its group), b2 [C]. Tap 0 takes the previous
+    token, tap 1 the current one. Reading: each convolution's output is rounded to the
+    act dtype (separate modules); the two-slot state holds (x_{t-1}, y1_{t-1}).
+    Returns y2 [S, C] and the new state (x_{S-1}, y1_{S-1}).
+    """
+    S, C = cin.shape
+    x = np.concatenate([f64(x_prev)[None], f64(cin)], axis=0)  # rows t = -1 .. S-1
+    w1 = f64(w1)
+    y1 = rnd(f64(b1)[None] + w1[:, 0][None] * x[0:S] + w1[:, 1][None] * x[1:S + 1])
+    y1e = np.concatenate([f64(y1_prev)[None], y1], axis=0)  # rows t = -1 .. S-1
+    gs = C // groups
+    y2 = np.empty((S, C))
+    w2 = f64(w2)
+    for g in range(groups):
+        cs = slice(g * gs, (g + 1) * gs)
+        y2[:, cs] = f64(b2)[cs][None] + y1e[0:S, cs] @ w2[cs, 0, :].T + y1e[1:S + 1, cs] @ w2[cs, 1, :].T
+    return rnd(y2), x[S], y1e[S]
+
+
 def rope_rotate(x, pos, rope_dim, theta):
     """Rotary embedding on the first ``rope_dim`` dims of the last axis (rotate-half pairing).
 
@@ -208,7 +237,8 @@ def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd):
     """Queries, keys and values of the CCA projection for B sequences.
 
     xn: [B, S, H] normed input (act values). cache_len: [B] ints. conv_state:
-    [B, C, 2] (slot 0 = t-2, slot 1 = t-1). prev_hs: [B, H] the previous token's
+    [B, C, 2] (kernel 3: slot 0 = input t-2, slot 1 = input t-1; the two-stage form,
+    conv_k = 2: slot 0 = input t-1, slot 1 = depthwise output t-1). prev_hs: [B, H] the previous token's
     normed input. A sequence with cache_len 0 is fresh: its history is zero
     whatever the state buffers hold (reading).
 
@@ -246,7 +276,12 @@ def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd):
         fresh = int(cache_len[b]) == 0
         hist = np.zeros((2, C)) if fresh else f64(conv_state[b]).T  # [2, C]
         cin = np.concatenate([Pq[b].reshape(S, nh * d), Pk[b].reshape(S, nkv * d)], axis=1)
-        y, ext = causal_conv3(cin, hist, w["conv_w"], w["conv_b"])
+        if cfg.conv_k == 2:  # the printout's two kernel-2 convolutions; state = (x_{t-1}, y1_{t-1})
+            y, xl, y1l = causal_conv_two_stage(cin, hist[0], hist[1], w["conv_w"], w["conv_b"], w["conv2_w"],
+                                               w["conv2_b"], nh + nkv, rnd)
+            ext = np.concatenate([np.zeros((S, C)), xl[None], y1l[None]], axis=0)  # new state rows S, S+1
+        else:
+            y, ext = causal_conv3(cin, hist, w["conv_w"], w["conv_b"])
         yq = y[:, :nh * d].reshape(S, nh, d)
         yk = y[:, nh * d:].reshape(S, nkv, d)
         # residual (reading: the pre-conv projections are averaged; g(h) = h // G)

@@ -42,7 +42,7 @@ class BlockConfig(C.Structure):
 
 WEIGHT_FIELDS = ("ln1_g", "W_qkv", "conv_w", "conv_b", "temp", "W_o", "a_hsb", "a_hss", "a_rb", "a_rs", "ln2_g",
                  "r_Wd", "r_bd", "r_rss", "r_norm_g", "r_W1", "r_b1", "r_W2", "r_b2", "r_Wout", "bal_bias", "W_gu",
-                 "W_dn", "m_hsb", "m_hss", "m_rb", "m_rs", "W_gu_scale", "W_dn_scale")
+                 "W_dn", "m_hsb", "m_hss", "m_rb", "m_rs", "W_gu_scale", "W_dn_scale", "conv2_w", "conv2_b")
 
 
 class BlockWeights(C.Structure):

@@ -32,9 +32,12 @@ constexpr int kCcaRows = kCcaTokens + 2;  // the tile plus two tokens of history
 //   xs[r][G*d .. (G+1)*d)  k channels of the group's key head
 //   xs[r][(G+1)*d .. +d/2) v_current half of the group
 //   xs[r][.. +d/2)          v_delayed half of the group
+// With the printout's two convolutions (TWO: conv_k == 2) the convolved q/k channels
+// come precomputed (conv2_kernel below) and one more buffer follows:
+//   y2s[m][0 .. GC)  the two-stage conv output of token t0 + m
 // D (head_dim) and GG (query heads per KV head) are compile-time, so the per-head
 // loops unroll and the head norms' cross-lane reductions run side by side.
-template <typename T, int D, int GG>
+template <typename T, int D, int GG, bool TWO>
 __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   extern __shared__ __attribute__((aligned(16))) char cca_lds[];
   const int b = blockIdx.z, g = blockIdx.y, tile = blockIdx.x;
@@ -48,6 +51,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   T* outs = reinterpret_cast<T*>(reinterpret_cast<char*>(wsm) + GC * 4 * sizeof(float));
   // outs: per wave, the rows of the token(s) of one step (G query heads, key, value)
   // gathered so they leave in 16-byte stores
+  T* y2s = outs + 4 * (128 / d) * (G + 2) * d;
   const int S = a.S, QR = a.qkv_ld;
   const int kcol = nh * d, vccol = nh * d + nkv * d, vdcol = vccol + nkv * d / 2;
   const int L0 = a.cache_len[b];
@@ -116,6 +120,24 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         if (ch < nrows * per_row && t >= 0) *reinterpret_cast<u32x4*>(xs + rr * ROWE + dst) = val[k];
       }
     }
+    if (TWO) {  // the tile's two-stage conv outputs (q then k channels of the group)
+      const int per_y = segq + segk;
+      const int ny = (t_end - t0) * per_y;
+      for (int c0 = threadIdx.x; c0 < ny; c0 += kBatch * nthr) {
+        u32x4 val[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int ch = c0 + k * nthr, cc = ch % per_y;
+          const int src = cc < segq ? g * G * d + cc * E16 : kcol + g * d + (cc - segq) * E16;
+          if (ch < ny) val[k] = *reinterpret_cast<const u32x4*>(a.y2 + ((size_t)b * S + t0 + ch / per_y) * a.C + src);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int ch = c0 + k * nthr;
+          if (ch < ny) *reinterpret_cast<u32x4*>(y2s + (ch / per_y) * GC + (ch % per_y) * E16) = val[k];
+        }
+      }
+    }
     // history (tokens -2, -1 of a sequence with cached tokens): q/k channels from
     // conv_state, the delayed value from prev_hs @ W_vd^T
     if (t0 == 0) {
@@ -125,7 +147,10 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         for (int k = 0; k < kBatch; ++k) {
           const int i = i0 + k * nthr;
           const int rr = i / GC, c = i % GC;
-          hv[k] = (fresh || i >= 2 * GC) ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + rr];
+          // kernel 3: rows -2, -1 are slots 0, 1. Two stages: row -1 is slot 0 (the input
+          // one token back), used for the new state
+          const bool none = fresh || i >= 2 * GC || (TWO && rr == 0);
+          hv[k] = none ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + (TWO ? 0 : rr)];
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -143,10 +168,17 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       for (int k = 0; k < 2; ++k) {
         const int c = c0 + k * nthr;
         const int gc = gchan(min(c, GC - 1));
-        wv[k][0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
-        wv[k][1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
-        wv[k][2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
-        wv[k][3] = Act<T>::tof(a.conv_b[gc]);
+        if (TWO) {  // depthwise taps (previous, current) and bias: the new state's slot 1
+          wv[k][0] = Act<T>::tof(a.conv_w[gc * 2 + 0]);
+          wv[k][1] = Act<T>::tof(a.conv_w[gc * 2 + 1]);
+          wv[k][2] = Act<T>::tof(a.conv_b[gc]);
+          wv[k][3] = 0.f;
+        } else {
+          wv[k][0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
+          wv[k][1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
+          wv[k][2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
+          wv[k][3] = Act<T>::tof(a.conv_b[gc]);
+        }
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -178,6 +210,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
     const T* x1 = x0 - ROWE;       // t - 1
     const T* x2 = x1 - ROWE;       // t - 2
     auto conv = [&](int c) -> float {
+      if constexpr (TWO) return Act<T>::tof(y2s[(tt - t0) * GC + c]);
       const float* w = wsm + c * 4;
       return w[3] + w[0] * Act<T>::tof(x2[c]) + w[1] * Act<T>::tof(x1[c]) + w[2] * Act<T>::tof(x0[c]);
     };
@@ -281,7 +314,18 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       const int gc = gchan(c);
       T* cs = a.conv_state + ((size_t)b * a.C + gc) * 2;
       T s0, s1;
-      if (t_end == S) {  // one tile: rows S-2 (or the history row) and S-1 are in LDS
+      if (TWO) {  // (input of token S-1, depthwise output of token S-1)
+        if (t_end == S) {  // LDS rows S, S+1 are tokens S-2 (the old slot 0 when S = 1), S-1
+          const float* w = wsm + c * 4;
+          s0 = xs[(S + 1) * ROWE + c];
+          s1 = Act<T>::cvt(w[2] + w[0] * Act<T>::tof(xs[S * ROWE + c]) + w[1] * Act<T>::tof(s0));
+        } else {
+          const float* w = wsm + c * 4;
+          s0 = a.P[((size_t)b * S + S - 1) * QR + gc];
+          s1 = Act<T>::cvt(w[2] + w[0] * Act<T>::tof(a.P[((size_t)b * S + S - 2) * QR + gc]) +
+                           w[1] * Act<T>::tof(s0));
+        }
+      } else if (t_end == S) {  // one tile: rows S-2 (or the history row) and S-1 are in LDS
         s0 = xs[S * ROWE + c];
         s1 = xs[(S + 1) * ROWE + c];
       } else {
@@ -301,23 +345,258 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   }
 }
 
-size_t cca_lds_bytes(int d, int G, int act_bytes) {
+// ---- the two-stage q/k convolution ("Printout": conv_qk_depthwise then conv_qk_grouped)
+//
+// One workgroup per (64-row tile of the B*S tokens, head h). Thread (chunk, row group)
+// reads the inputs of 8 channels of its rows and the two rows before them straight into
+// registers and forms, per row, z = [y1(t-1) | y1(t)] (2d values, each depthwise output
+// rounded to T; y1(t-1) of one row is y1(t) of the row before it when both are in the
+// same sequence). z goes to LDS; y2 = rnd(b2 + W2_h z) is then a [64 x 2d] x [2d x d]
+// product on MFMA: wave w takes d/4 output channels, whose weight rows (the first
+// operand) it loads once into registers, and all four 16-row blocks of z (the second
+// operand) per k-step, so eight accumulations are in flight.
+constexpr int kC2Rows = 64;
+
+// Eight act values kept as loaded (16 bytes of bf16, 32 of fp32) and widened on use.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ float operator[](int k) const {
+    const uint32_t u = w[k >> 1];
+    return __uint_as_float((k & 1) ? (u & 0xFFFF0000u) : (u << 16));
+  }
+};
+template <> struct Raw8<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = reinterpret_cast<const float4*>(p)[0];
+    hi = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ float operator[](int k) const {
+    const float4& q = k < 4 ? lo : hi;
+    switch (k & 3) { case 0: return q.x; case 1: return q.y; case 2: return q.z; default: return q.w; }
+  }
+};
+
+// Eight floats rounded to the act type (round to nearest even) in their stored form.
+template <typename T> struct Pack8;
+template <> struct Pack8<bf16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void set(const float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  }
+  __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void store(bf16_t* p) const { *reinterpret_cast<u32x4*>(p) = w; }
+};
+template <> struct Pack8<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void set(const float* v) {
+    lo = make_float4(v[0], v[1], v[2], v[3]);
+    hi = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __device__ __forceinline__ void zero() { lo = hi = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<float4*>(p)[0] = lo;
+    reinterpret_cast<float4*>(p)[1] = hi;
+  }
+};
+// Four floats rounded to the act type and stored (8 bytes of bf16, 16 of fp32).
+__device__ __forceinline__ void store4_rne(bf16_t* p, const float* v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ void store4_rne(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void conv2_kernel(Conv2Args<T> a) {
+  extern __shared__ __attribute__((aligned(16))) char c2_lds[];
+  constexpr int d = D, K2 = 2 * D;
+  constexpr int ZP = K2 + 8;  // z row pitch: the 16 rows of a fragment load start 16 bytes apart
+  constexpr int OP = d + 8;   // output tile row pitch, same reason
+  constexpr int E16 = 16 / (int)sizeof(T);
+  constexpr int CPW = d / 4, NJ = CPW / 16, NKS = K2 / 32;
+  constexpr int NCH = d / 8, RG = 256 / NCH, RPG = kC2Rows / RG;  // 8-channel chunks, row groups
+  T* z = reinterpret_cast<T*>(c2_lds);  // [kC2Rows][ZP]; later the output tile [kC2Rows][OP]
+  using MF = Mfma<T>;
+  const int h = blockIdx.y, r0 = blockIdx.x * kC2Rows;
+  const int S = a.S, C = a.C, QR = a.qkv_ld, rows = a.B * S;
+  const int nrow = min(kC2Rows, rows - r0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int ch = threadIdx.x % NCH, rg = threadIdx.x / NCH;
+  const int c = ch * 8, m0 = rg * RPG;
+
+  // every load is issued up front, with indices clamped into range (no load behind a
+  // branch): this thread's input rows r0+m0-2 .. r0+m0+RPG-1, taps, the cache length
+  // of each row's sequence
+  Raw8<T> x[RPG + 2];
+#pragma unroll
+  for (int i = 0; i < RPG + 2; ++i) {
+    const int r = min(max(r0 + m0 - 2 + i, 0), rows - 1);
+    x[i].load(a.P + (size_t)r * QR + h * d + c);
+  }
+  Raw8<T> tw[2], b1;  // taps (previous, current) of the 8 channels, interleaved; bias
+  tw[0].load(a.conv_w + (size_t)(h * d + c) * 2);
+  tw[1].load(a.conv_w + (size_t)(h * d + c) * 2 + 8);
+  b1.load(a.conv_b + h * d + c);
+  int cl[RPG];
+#pragma unroll
+  for (int j = 0; j < RPG; ++j) cl[j] = a.cache_len[min(r0 + m0 + j, rows - 1) / S];
+
+  // z rows of this thread (rows past the tile are zero)
+  Pack8<T> prev, cur;
+  auto dw = [&](auto xm1, auto x0, Pack8<T>& y) {  // depthwise output (xm1, x0: k -> value)
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = b1[k] + tw[k >> 2][2 * (k & 3)] * xm1(k) + tw[k >> 2][2 * (k & 3) + 1] * x0(k);
+    y.set(v);
+  };
+  auto row = [&](int i) { return [&x, i](int k) { return x[i][k]; }; };
+#pragma unroll
+  for (int j = 0; j < RPG; ++j) {
+    const int m = m0 + j, r = r0 + m;
+    const int t = r - (r / S) * S;
+    if (m < nrow) {
+      if (t >= 2) {
+        if (j == 0) dw(row(j), row(j + 1), prev);
+        else prev = cur;  // y1(t-1) = the previous row's y1(t)
+        dw(row(j + 1), row(j + 2), cur);
+      } else {  // the history comes from the state: slot 0 = input, slot 1 = depthwise output
+        Raw8<T> sv[2];
+        const bool hist = cl[j] != 0;
+        if (hist) {
+          const T* st = a.conv_state + ((size_t)(r / S) * C + h * d + c) * 2;
+          sv[0].load(st);
+          sv[1].load(st + 8);
+        }
+        auto xm1 = [&](int k) { return hist ? sv[k >> 2][2 * (k & 3)] : 0.f; };
+        if (t == 0) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = hist ? sv[k >> 2][2 * (k & 3) + 1] : 0.f;
+          prev.set(v);  // already act values: exact
+          dw(xm1, row(j + 2), cur);
+        } else {
+          dw(xm1, row(j + 1), prev);
+          dw(row(j + 1), row(j + 2), cur);
+        }
+      }
+    } else {
+      prev.zero();
+      cur.zero();
+    }
+    prev.store(z + m * ZP + c);
+    cur.store(z + m * ZP + d + c);
+  }
+  // this wave's weight fragments, requested before the barrier (fewer registers live
+  // while z is formed; other workgroups on the CU cover the wait)
+  typename MF::frag wf[NJ][NKS];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const T* wrow = a.conv2_w + (size_t)(h * d + wave * CPW + j * 16 + r16) * K2 + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) wf[j][ks] = MF::load(wrow + ks * 32);
+  }
+  __syncthreads();
+
+  f32x4 acc[NJ][kC2Rows / 16];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int mt = 0; mt < kC2Rows / 16; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    typename MF::frag zf[kC2Rows / 16];
+#pragma unroll
+    for (int mt = 0; mt < kC2Rows / 16; ++mt) zf[mt] = MF::load(z + (mt * 16 + r16) * ZP + ks * 32 + grp * 8);
+#pragma unroll
+    for (int mt = 0; mt < kC2Rows / 16; ++mt)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j][mt] = MF::mma(wf[j][ks], zf[mt], acc[j][mt]);
+  }
+  float b2[NJ][4];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) load4(a.conv2_b + h * d + wave * CPW + j * 16 + 4 * grp, b2[j]);
+  __syncthreads();  // z becomes the output tile
+#pragma unroll
+  for (int mt = 0; mt < kC2Rows / 16; ++mt)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {  // lane holds channels co .. co+3 of row mt*16 + r16
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = acc[j][mt][i] + b2[j][i];
+      store4_rne(z + (mt * 16 + r16) * OP + wave * CPW + j * 16 + 4 * grp, v);
+    }
+  __syncthreads();
+  constexpr int per_row = d / E16;
+  for (int q = threadIdx.x; q < nrow * per_row; q += 256) {
+    const int m = q / per_row, cc = (q % per_row) * E16;
+    *reinterpret_cast<u32x4*>(a.y2 + (size_t)(r0 + m) * C + h * d + cc) =
+        *reinterpret_cast<const u32x4*>(z + m * OP + cc);
+  }
+}
+
+size_t conv2_lds_bytes(int d, int act_bytes) { return (size_t)kC2Rows * (2 * d + 8) * act_bytes; }
+
+// dynamic LDS the conv2 launches may ask for (fp32, d = 128 needs ~103 KB); the kernel's
+// static row tables come on top, within the CU's 160 KB
+constexpr int kC2MaxLds = 128 * 1024;
+
+template <typename T>
+hipError_t launch_conv2(const Conv2Args<T>& a, hipStream_t s) {
+  const int rows = a.B * a.S;
+  dim3 grid((rows + kC2Rows - 1) / kC2Rows, a.C / a.d);
+  const size_t lds = conv2_lds_bytes(a.d, (int)sizeof(T));
+  if (a.d == 128) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)conv2_kernel<T, 128>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kC2MaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((conv2_kernel<T, 128>), grid, dim3(256), lds, s, a);
+  } else if (a.d == 64) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)conv2_kernel<T, 64>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kC2MaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((conv2_kernel<T, 64>), grid, dim3(256), lds, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_conv2<bf16_t>(const Conv2Args<bf16_t>&, hipStream_t);
+template hipError_t launch_conv2<float>(const Conv2Args<float>&, hipStream_t);
+
+size_t cca_lds_bytes(int d, int G, int act_bytes, bool two) {
   const int GC = (G + 1) * d;
   const size_t xs = ((size_t)kCcaRows * (GC + d) * act_bytes + 15) & ~(size_t)15;
   const size_t outs = (size_t)4 * (128 / d) * (G + 2) * d * act_bytes;  // 4 waves x tokens per step
-  return xs + (size_t)GC * 4 * sizeof(float) + outs;
+  const size_t y2 = two ? (size_t)kCcaTokens * GC * act_bytes : 0;
+  return xs + (size_t)GC * 4 * sizeof(float) + outs + y2;
+}
+
+template <typename T, int DD, int GG>
+static hipError_t launch_cca_dg(const CcaArgs<T>& a, dim3 grid, hipStream_t s) {
+  const size_t lds = cca_lds_bytes(DD, GG, (int)sizeof(T), a.conv_k == 2);
+  if (a.conv_k == 2) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)cca_kernel<T, DD, GG, true>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((cca_kernel<T, DD, GG, true>), grid, dim3(256), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((cca_kernel<T, DD, GG, false>), grid, dim3(256), lds, s, a);
+  }
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s) {
   dim3 grid((a.S + kCcaTokens - 1) / kCcaTokens, a.nkv, a.B);
   const int G = a.nh / a.nkv;
-  const size_t lds = cca_lds_bytes(a.d, G, (int)sizeof(T));
-#define ZAYA_CCA_CASE(DD, GG)                                                      \
-  if (a.d == DD && G == GG) {                                                      \
-    hipLaunchKernelGGL((cca_kernel<T, DD, GG>), grid, dim3(256), lds, s, a);        \
-    return hipGetLastError();                                                      \
-  }
+#define ZAYA_CCA_CASE(DD, GG) \
+  if (a.d == DD && G == GG) return launch_cca_dg<T, DD, GG>(a, grid, s);
   ZAYA_CCA_CASE(128, 1) ZAYA_CCA_CASE(128, 2) ZAYA_CCA_CASE(128, 4) ZAYA_CCA_CASE(128, 8)
   ZAYA_CCA_CASE(64, 1) ZAYA_CCA_CASE(64, 2) ZAYA_CCA_CASE(64, 4) ZAYA_CCA_CASE(64, 8)
 #undef ZAYA_CCA_CASE

@@ -51,9 +51,33 @@ struct CcaArgs {
   T* v_tap;
   int B, S, H, nh, nkv, d, rope_dim, C;
   float theta;
+  int conv_k = 3;         // 3: one depthwise conv; 2: depthwise k2 then grouped k2
+  const T* y2 = nullptr;  // conv_k == 2: the convolved q/k channels [B*S][C] (launch_conv2)
 };
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s);
+
+// The printout's two-stage q/k convolution (conv_k == 2) of every token: depthwise
+// kernel 2 (conv_w [C][2], conv_b), then grouped kernel 2 with one group per head
+// (conv2_w [C][2][d], conv2_b), each output rounded to T. History from conv_state
+// (slot 0 = input, slot 1 = depthwise output, one token back), zeros when fresh.
+template <typename T>
+struct Conv2Args {
+  const T* P;  // [B*S][qkv_ld]: columns 0 .. C are the q then k channels
+  int qkv_ld;
+  const T* conv_w;
+  const T* conv_b;
+  const T* conv2_w;
+  const T* conv2_b;
+  const T* conv_state;  // [B][C][2]
+  const int32_t* cache_len;
+  T* y2;  // [B*S][C]
+  int B, S, C, d;
+};
+template <typename T>
+hipError_t launch_conv2(const Conv2Args<T>& a, hipStream_t s);
+// dynamic LDS of one CCA workgroup (two: the two-stage convolution)
+size_t cca_lds_bytes(int d, int G, int act_bytes, bool two);
 
 // ---- attention
 template <typename T>

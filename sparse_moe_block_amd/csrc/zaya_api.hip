@@ -50,7 +50,10 @@ int check_config(const zaya_block_config* c) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ZAYA_ESHAPE, "n_heads / n_kv_heads = %d not in {1,2,4,8}", G);
   if (c->rope_dim < 0 || c->rope_dim > c->head_dim || (c->rope_dim & 1))
     return fail(ZAYA_ESHAPE, "rope_dim %d must be even and <= head_dim", c->rope_dim);
-  if (c->conv_k != 3) return fail(ZAYA_ESHAPE, "conv_k %d != 3", c->conv_k);
+  if (c->conv_k != 3 && c->conv_k != 2) return fail(ZAYA_ESHAPE, "conv_k %d not in {2, 3}", c->conv_k);
+  if (c->conv_k == 2 && cca_lds_bytes(c->head_dim, G, (int)act_bytes(c), true) > 160 * 1024)
+    return fail(ZAYA_ESHAPE, "conv_k 2: head_dim %d with %d query heads per key head does not fit LDS in this dtype",
+                c->head_dim, G);
   if (c->n_experts + 1 > 32) return fail(ZAYA_ESHAPE, "n_experts + 1 > 32");
   if (c->hidden % 256 || c->hidden > 4096) return fail(ZAYA_ESHAPE, "hidden %d must be a multiple of 256, <= 4096", c->hidden);
   if (c->expert_inter % 64) return fail(ZAYA_ESHAPE, "expert_inter %d must be a multiple of 64", c->expert_inter);
@@ -75,7 +78,8 @@ int prefill_chunks_ws(const zaya_block_config* c, int S) {
 
 // Workspace layout of one block call.
 struct Plan {
-  size_t cache_len, xn, P, vdp, Q, Kw, Vw, convw, prevw, O, h, hn, logits, cls, idx, wts, offsets, ids, neurons, part;
+  size_t cache_len, xn, P, vdp, y2, Q, Kw, Vw, convw, prevw, O, h, hn, logits, cls, idx, wts, offsets, ids, neurons,
+      part;
   size_t gpart, gpart_bytes;  // split-K partials of the few-row GEMMs
   size_t total;
 };
@@ -98,6 +102,7 @@ Plan plan_block(const zaya_block_config* c, int B, int S, int decode) {
   p.xn = take(T * H * A);
   p.P = take(T * QR * A);
   p.vdp = take((size_t)B * nkv * (d / 2) * A);
+  p.y2 = take(c->conv_k == 2 ? T * C * A : 0);  // two-stage conv output
   p.Q = take(T * nh * d * A);
   p.Kw = take(T * nkv * d * A);  // keys/values when the caller passes no cache
   p.Vw = take(T * nkv * d * A);
@@ -134,6 +139,8 @@ int check_weights(const zaya_block_config* c, const zaya_block_weights* w) {
   if (!w) return fail(ZAYA_EINVAL, "weights is NULL");
   if (c->expert_format == ZAYA_EXPERTS_FP8_E4M3 && (!w->W_gu_scale || !w->W_dn_scale))
     return fail(ZAYA_EINVAL, "FP8 experts need W_gu_scale and W_dn_scale");
+  if (c->conv_k == 2 && (!w->conv2_w || !w->conv2_b))
+    return fail(ZAYA_EINVAL, "conv_k 2 needs conv2_w and conv2_b");
   const void* ptrs[] = {w->ln1_g, w->W_qkv, w->conv_w, w->conv_b, w->temp, w->W_o, w->a_hsb, w->a_hss, w->a_rb,
                         w->a_rs, w->ln2_g, w->r_Wd, w->r_bd, w->r_rss, w->r_norm_g, w->r_W1, w->r_b1, w->r_W2,
                         w->r_b2, w->r_Wout, w->bal_bias, w->W_gu, w->W_dn, w->m_hsb, w->m_hss, w->m_rb, w->m_rs};
@@ -217,9 +224,16 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
     HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, gpart, p.gpart_bytes, st));
   // a3: convolution, residual, QK norm, temperature, rotary, value halves, state
   HIPCHK(mark(2));
+  T* y2 = nullptr;
+  if (c->conv_k == 2) {  // the two-stage conv first: it reads conv_state before the CCA kernel updates it
+    y2 = (T*)(ws + p.y2);
+    Conv2Args<T> c2{P, QR, W(w->conv_w), W(w->conv_b), W(w->conv2_w), W(w->conv2_b), conv_state, cl_dev, y2,
+                    B, S, C, d};
+    HIPCHK(launch_conv2<T>(c2, st));
+  }
   CcaArgs<T> ca{P, QR, vdp, W(w->conv_w), W(w->conv_b), W(w->temp), conv_state, prev_hs, xn, cl_dev, Q, Kc, Vc, cap,
                 (T*)tp.attention_queries, (T*)tp.attention_keys, (T*)tp.attention_values,
-                B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta};
+                B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta, c->conv_k, y2};
   HIPCHK(launch_cca<T>(ca, st));
   // a4: attention
   HIPCHK(mark(3));

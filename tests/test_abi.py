@@ -79,7 +79,8 @@ BAD_CONFIGS = [
     (dict(num_heads=6, num_kv_heads=2), -2, "n_heads"),  # group of 3
     (dict(rope_dim=63), -2, "rope_dim"),
     (dict(rope_dim=256), -2, "rope_dim"),
-    (dict(conv_k=2), -2, "conv_k"),
+    (dict(conv_k=4), -2, "conv_k"),
+    (dict(conv_k=2, act_dtype="f32", head_dim=128, num_heads=16, num_kv_heads=2), -2, "LDS"),
     (dict(num_experts=32), -2, "n_experts"),
     (dict(hidden_size=2000), -2, "hidden"),
     (dict(moe_intermediate_size=2000), -2, "expert_inter"),
@@ -162,8 +163,20 @@ def test_fp8_experts_validation(L):
     assert _prefill(L, _args(cfg, 1, 8, ws_bytes=0)) == -4
     # act-format experts ignore the scale pointers
     fields = [FAKE] * len(Z.WEIGHT_FIELDS)
-    fields[-1] = fields[-2] = None
+    fields[Z.WEIGHT_FIELDS.index("W_gu_scale")] = fields[Z.WEIGHT_FIELDS.index("W_dn_scale")] = None
     assert _prefill(L, _args(CONFIGS["prefill"], 1, 8, w=C.byref(Z.BlockWeights(*fields)), ws_bytes=0)) == -4
+
+
+def test_two_stage_conv_validation(L):
+    # conv_k 2 needs the grouped stage's weight and bias; conv_k 3 ignores them
+    cfg = CONFIGS["prefill"].replace(conv_k=2)
+    for name in ("conv2_w", "conv2_b"):
+        fields = [FAKE] * len(Z.WEIGHT_FIELDS)
+        fields[Z.WEIGHT_FIELDS.index(name)] = None
+        rc = _prefill(L, _args(cfg, 1, 8, w=C.byref(Z.BlockWeights(*fields)), ws_bytes=0))
+        assert rc == -1 and "conv2" in L.zaya_last_error().decode()
+        assert _prefill(L, _args(CONFIGS["prefill"], 1, 8, w=C.byref(Z.BlockWeights(*fields)), ws_bytes=0)) == -4
+    assert _prefill(L, _args(cfg, 1, 8, ws_bytes=0)) == -4
 
 
 def test_cache_bounds_are_checked(L):

@@ -54,6 +54,28 @@ def test_bf16_decode_small():
     _full_check(CONFIGS["decode"].replace(name="decode_small", batch=5, kv_len=333))
 
 
+# The two-stage conv (conv_k 2): depthwise taps at unit scale (std 0.33); the grouped
+# stage sums 2 * head_dim inputs, so its unit-gain draw has std 1/sqrt(2 d) (0.0625 at
+# d = 128). The fp32 case also runs a gain-5 grouped stage (std 0.33) at fp32 tolerance.
+def test_tiny_fp32_two_stage_conv():
+    _full_check(CONFIGS["tiny"].replace(name="tiny_conv2", conv_k=2, conv_std=0.33, conv2_std=0.33, seq=50,
+                                        batch=2))
+
+
+def test_bf16_two_stage_conv_ragged():
+    _full_check(small_bf16(name="small_conv2", conv_k=2, conv_std=0.33, conv2_std=0.0625))
+
+
+def test_bf16_two_stage_conv_chunked_with_cache():
+    _full_check(small_bf16(name="small_conv2_cached", conv_k=2, conv_std=0.33, conv2_std=0.0625, seq=77, batch=3,
+                           kv_len=130))
+
+
+def test_bf16_two_stage_conv_decode():
+    _full_check(CONFIGS["decode"].replace(name="decode_conv2", conv_k=2, conv_std=0.33, conv2_std=0.0625, batch=5,
+                                          kv_len=333))
+
+
 def test_deterministic_rerun():
     cfg = small_bf16(name="small_det", seq=150)
     a = BlockRun(cfg).run()

@@ -186,6 +186,22 @@ def check_taps(run: BlockRun, ref: dict, skip=()) -> dict:
     routed_rows = rows[pos[rows] >= 0]
     if len(routed_rows):
         g = to_np(t["mlp_neurons"])[pos[routed_rows]]
+        # Stage-local: the oracle's expert on the GPU's own MoE input rows. The neurons pass
+        # four act-dtype roundings (gate, up, activation, product), which turn one-ulp
+        # differences upstream into several ulps at |x| ~ 1; end to end they are held to the
+        # relative RMS bound, and the block's outputs above to both bounds.
+        w = np_weights(run.w_host)
+        xin = to_np(t["mlp_norm_output"]).reshape(B * S, H)[routed_rows]
+        cls = t["expert_classes"].cpu().numpy().reshape(-1)[routed_rows]
+        loc = np.empty_like(g)
+        rnd = O.rounder(act)
+        for e in np.unique(cls):
+            sel = cls == e
+            loc[sel] = O.expert(cfg, w, int(e), xin[sel], rnd)[1]
+        res["mlp_neurons"] = compare("mlp_neurons", g, loc, act)
         r = ref["mlp_neurons"][np.searchsorted(rows, routed_rows)]
-        res["mlp_neurons"] = compare("mlp_neurons", g, r, act)
+        err = np.abs(g - r)
+        e2e = float(np.sqrt(np.mean(err * err)) / max(float(np.sqrt(np.mean(r * r))), 1e-30))
+        assert e2e <= TOL[act][1], f"mlp_neurons end to end: relative RMS error {e2e:.3e} > {TOL[act][1]}"
+        res["mlp_neurons_e2e"] = {"max": float((err / np.maximum(1.0, np.abs(r))).max()), "rel_rms": e2e}
     return res

@@ -45,7 +45,7 @@ class ZayaConfig:
     act_dtype: str  # "bf16" or "f32"
     batch: int
     seq: int
-    conv_k: int = 3
+    conv_k: int = 3  # 3: one depthwise kernel-3 conv; 2: the printout's depthwise k2 then grouped k2
     rms_norm_eps: float = 1e-5
     sliding_window: int = -1  # < 0: off; else key visible iff p_q - p_k <= window
     kv_len: int = 0  # tokens already in the cache before this call
@@ -55,6 +55,7 @@ class ZayaConfig:
     has_router_state: bool = True  # False: block-0 semantics (no carried state)
     temp_range: tuple = (0.8, 2.0)  # key temperature drawn U(lo, hi); (1, 1) = ones
     conv_std: float = 0.02  # std of the conv taps and bias
+    conv2_std: float = 0.02  # std of the grouped conv stage's taps and bias (conv_k == 2)
     gain_std: float = 0.0  # RMSNorm gains: 1 + N(0, gain_std); 0 = ones
     bal_bias: str = "zeros"  # "zeros", "normal", "trained", "zipf"
     expert_format: str = "act"  # "act" or "fp8": expert weights stored as E4M3 bytes + fp32 row scales
@@ -103,6 +104,9 @@ CONFIGS: Dict[str, ZayaConfig] = {
     # the same decode step with the expert weights stored as FP8 E4M3 + fp32 row scales
     "decode_fp8": ZayaConfig(name="decode_fp8", **_full(batch=64, seq=1, kv_len=8192, decode=True,
                                                         expert_format="fp8")),
+    # the prefill workload with the printout's two-stage q/k convolution (depthwise k2, then
+    # grouped k2 with one group per head)
+    "prefill_conv2": ZayaConfig(name="prefill_conv2", **_full(batch=1, seq=4096, conv_k=2)),
     # 40-block stack prefill, bf16, B4 S2048, vocab 262144
     "stack": ZayaConfig(name="stack", **_full(batch=4, seq=2048, num_layers=40, vocab_size=262144)),
     # long-context prefill, bf16, B1 S32768, window 4096, Zipf(1.2) expert load + 15% skip
@@ -168,6 +172,7 @@ def block_weight_shapes(cfg: ZayaConfig) -> Dict[str, tuple]:
         "r_b1": (R,), "r_W2": (R, R), "r_b2": (R,), "r_Wout": (E + 1, R), "bal_bias": (E + 1,),
         "W_gu": (E, 2 * I, H), "W_dn": (E, H, I),
         "m_hsb": (H,), "m_hss": (H,), "m_rb": (H,), "m_rs": (H,),
+        **({"conv2_w": (C, 2, d), "conv2_b": (C,)} if cfg.conv_k == 2 else {}),
     }
 
 
@@ -220,6 +225,9 @@ def block_weights(cfg: ZayaConfig, block: int = 0, seed: int = 0,
         "m_rb": N("m_rb", (H,), std=0.01),
         "m_rs": N("m_rs", (H,), 1.0, 0.05),
     }
+    if cfg.conv_k == 2:  # grouped stage: [C, tap, d] (output channel, tap, input channel of its head)
+        w["conv2_w"] = N("conv2_w", (C, 2, d), std=cfg.conv2_std)
+        w["conv2_b"] = N("conv2_b", (C,), std=cfg.conv2_std)
     if bal_bias is not None:
         bb = np.asarray(bal_bias, np.float32)
     elif cfg.bal_bias == "normal":
@@ -293,6 +301,9 @@ def block_weights_device(cfg: ZayaConfig, block: int = 0, seed: int = 0, device=
         "m_rs": N("m_rs", 1.0, 0.05),
         "bal_bias": torch.zeros(shapes["bal_bias"], device=device, dtype=torch.float32),
     }
+    if cfg.conv_k == 2:
+        w["conv2_w"] = N("conv2_w", std=cfg.conv2_std)
+        w["conv2_b"] = N("conv2_b", std=cfg.conv2_std)
     return w
 
 
