@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ZAYA_ABI_VERSION 3
+#define ZAYA_ABI_VERSION 4
 
 enum zaya_dtype { ZAYA_F32 = 0, ZAYA_BF16 = 1 };
 
@@ -149,7 +149,14 @@ typedef struct zaya_block_weights {
  * conv_state and prev_hs are updated in place; cache_len is never written (the
  * caller advances it). cache_len is a host array (required); cache_len_dev is an
  * optional device copy of the same values (if NULL the library stages a copy in the
- * workspace with an asynchronous host-to-device copy). */
+ * workspace with an asynchronous host-to-device copy).
+ * ring != 0 makes K and V a ring buffer for a sliding-window block (the 74B preview's
+ * hybrid_sliding blocks, "Queries and keys are convolved ..." on the nnterp page): the
+ * token at position p lives in slot p % cap, so a window of W needs only cap = W + 1
+ * slots whatever the sequence length. It needs sliding_window >= 0 and cap >=
+ * sliding_window + 1; cache_len may then exceed cap. A prefill (S > 1) into a ring
+ * needs fresh sequences (every cache_len[b] == 0): the chunk's keys are formed in the
+ * workspace and the last min(S, cap) positions stored. */
 typedef struct zaya_cca_cache {
   void* K;
   void* V;
@@ -158,6 +165,7 @@ typedef struct zaya_cca_cache {
   void* prev_hs;
   const int32_t* cache_len;
   const int32_t* cache_len_dev;
+  int ring;
 } zaya_cca_cache;
 
 /* Optional debug taps, named after "The API / support()" on the nnterp page. Each
@@ -224,6 +232,10 @@ typedef struct zaya_stack_config {
   zaya_block_config block;
   int n_layers;
   int vocab;
+  /* Which blocks use block.sliding_window (the 74B preview's hybrid_sliding blocks are
+   * every other block, same page and section as the ring above): 0 = all of them; 1 =
+   * blocks 0, 2, 4, ... (the others attend to the whole prefix); 2 = blocks 1, 3, 5, ... */
+  int window_layers;
 } zaya_stack_config;
 
 /* embed [vocab, H] act (also the lm_head weight), emb_shift [H], emb_scale [H],

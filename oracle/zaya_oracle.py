@@ -587,6 +587,18 @@ def lm_head(cfg, sw, x_stream):
     return xf, linear(xf, sw["embed"], rnd)
 
 
+def layer_config(cfg, i):
+    """Block i's configuration in a stack. ("Queries and keys are convolved ...": the 74B
+    preview attends over a 4097-token window on its hybrid_sliding blocks, every other
+    block.) Reading: window_layers 1 windows blocks 0, 2, 4, ..., 2 windows blocks 1, 3,
+    5, ...; the other blocks attend to the whole prefix; 0 windows every block with
+    cfg.sliding_window (which may itself be off)."""
+    wl = getattr(cfg, "window_layers", 0)
+    if (wl == 1 and i % 2 == 1) or (wl == 2 and i % 2 == 0):
+        return cfg.replace(sliding_window=-1)
+    return cfg
+
+
 def stack_forward(cfg, sw, get_block, ids, caches=None):
     """Embedding, ``cfg.num_layers`` blocks with the router state carried from
     block to block (none into block 0), final norm and lm_head.
@@ -599,7 +611,7 @@ def stack_forward(cfg, sw, get_block, ids, caches=None):
     s = None
     for i in range(cfg.num_layers):
         c = None if caches is None else caches[i]
-        o = block_forward(cfg, get_block(i), x, s, c)
+        o = block_forward(layer_config(cfg, i), get_block(i), x, s, c)
         x = o["layer_output"].reshape(x.shape)
         s = o["router_state"].reshape(x.shape[0], x.shape[1], -1)
         res["layer_outputs"].append(x)

@@ -51,7 +51,8 @@ class BlockWeights(C.Structure):
 
 class CcaCache(C.Structure):
     _fields_ = [("K", C.c_void_p), ("V", C.c_void_p), ("cap", C.c_int), ("conv_state", C.c_void_p),
-                ("prev_hs", C.c_void_p), ("cache_len", C.POINTER(C.c_int32)), ("cache_len_dev", C.c_void_p)]
+                ("prev_hs", C.c_void_p), ("cache_len", C.POINTER(C.c_int32)), ("cache_len_dev", C.c_void_p),
+                ("ring", C.c_int)]
 
 
 TAP_FIELDS = ("attention_norm_output", "attention_queries", "attention_keys", "attention_values", "attention_premix",
@@ -65,7 +66,7 @@ class Taps(C.Structure):
 
 
 class StackConfig(C.Structure):
-    _fields_ = [("block", BlockConfig), ("n_layers", C.c_int), ("vocab", C.c_int)]
+    _fields_ = [("block", BlockConfig), ("n_layers", C.c_int), ("vocab", C.c_int), ("window_layers", C.c_int)]
 
 
 class StackWeights(C.Structure):
@@ -135,13 +136,15 @@ def block_weights(w: Mapping) -> BlockWeights:
 
 def cca_cache(cache: Optional[Mapping]):
     """(struct, keep-alive) from dict(K, V, conv_state, prev_hs, cache_len [host int list/tensor],
-    optional cache_len_dev [device int32 tensor])."""
+    optional cache_len_dev [device int32 tensor], optional ring [bool: K/V slots hold position p
+    at p % cap])."""
     if cache is None:
         return None, None
     lens = [int(v) for v in cache["cache_len"]]
     arr = (C.c_int32 * len(lens))(*lens)
     st = CcaCache(_ptr(cache["K"]), _ptr(cache["V"]), int(cache["K"].shape[2]), _ptr(cache["conv_state"]),
-                  _ptr(cache["prev_hs"]), C.cast(arr, C.POINTER(C.c_int32)), _ptr(cache.get("cache_len_dev")))
+                  _ptr(cache["prev_hs"]), C.cast(arr, C.POINTER(C.c_int32)), _ptr(cache.get("cache_len_dev")),
+                  int(bool(cache.get("ring", False))))
     return st, arr
 
 
@@ -177,7 +180,7 @@ def zaya_block_workspace_bytes(cfg, B: int, S: int, decode: bool = False) -> int
 
 
 def zaya_stack_workspace_bytes(cfg, B: int, S: int) -> int:
-    sc = StackConfig(block_config(cfg), cfg.num_layers, cfg.vocab_size)
+    sc = StackConfig(block_config(cfg), cfg.num_layers, cfg.vocab_size, getattr(cfg, "window_layers", 0))
     return int(lib().zaya_stack_workspace_bytes(C.byref(sc), B, S))
 
 
@@ -212,7 +215,7 @@ def zaya_stack_forward(cfg, sw: Mapping, blocks: Sequence[Mapping], B: int, S: i
                        workspace=None, stream=None) -> None:
     """Embedding, ``cfg.num_layers`` blocks, final norm and tied lm_head (see include/zaya.h)."""
     L = lib()
-    sc = StackConfig(block_config(cfg), cfg.num_layers, cfg.vocab_size)
+    sc = StackConfig(block_config(cfg), cfg.num_layers, cfg.vocab_size, getattr(cfg, "window_layers", 0))
     bw = (BlockWeights * len(blocks))(*[block_weights(b) for b in blocks])
     swt = StackWeights(_ptr(sw["embed"]), _ptr(sw["emb_shift"]), _ptr(sw["emb_scale"]), _ptr(sw["final_g"]),
                        C.cast(bw, C.POINTER(BlockWeights)))

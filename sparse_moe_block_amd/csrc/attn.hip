@@ -451,7 +451,9 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   const int kvalid = L0 + 1;
   const int W = a.window;
   const int klo = W >= 0 ? max(0, qp - W) : 0;
-  const int c_lo = max(klo, c * chunk), c_hi = min(kvalid, (c + 1) * chunk);
+  // chunks tile the visible range from the 64-aligned position at or below its start
+  const int kbase = (klo / 64) * 64;
+  const int c_lo = max(klo, kbase + c * chunk), c_hi = min(kvalid, kbase + (c + 1) * chunk);
   const float sscale = kLog2e / sqrtf((float)D);
 
   for (int i = lane; i < D; i += 64) q_s[wave][i] = Act<T>::tof(a.Q[((size_t)b * a.nh + h) * D + i]);
@@ -474,8 +476,9 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
       const int ch = threadIdx.x + i * NT;
       const int key = ch / CPR, col = (ch % CPR) * E16;
       const bool ok = ch < NCH && t0 + key < c_hi;
-      kr[i] = ok ? *reinterpret_cast<const uint4*>(Kb + (size_t)(t0 + key) * D + col) : make_uint4(0, 0, 0, 0);
-      vr[i] = ok ? *reinterpret_cast<const uint4*>(Vb + (size_t)(t0 + key) * D + col) : make_uint4(0, 0, 0, 0);
+      const size_t slot = a.ring ? (size_t)((t0 + key) % a.cap) : (size_t)(t0 + key);  // ring: p % cap
+      kr[i] = ok ? *reinterpret_cast<const uint4*>(Kb + slot * D + col) : make_uint4(0, 0, 0, 0);
+      vr[i] = ok ? *reinterpret_cast<const uint4*>(Vb + slot * D + col) : make_uint4(0, 0, 0, 0);
     }
   };
   const int t_first = (c_lo / 64) * 64;
@@ -601,10 +604,10 @@ static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, h
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_decode_dg(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s) {
-  int nchunk = min(kDecChunksMax, (maxlen + kDecChunkMin - 1) / kDecChunkMin);
-  const int chunk = (((maxlen + nchunk - 1) / nchunk) + 63) / 64 * 64;
-  nchunk = (maxlen + chunk - 1) / chunk;
+static hipError_t launch_decode_dg(const AttnArgs<T>& a, float* part, int span, hipStream_t s) {
+  int nchunk = min(kDecChunksMax, (span + kDecChunkMin - 1) / kDecChunkMin);
+  const int chunk = (((span + nchunk - 1) / nchunk) + 63) / 64 * 64;
+  nchunk = (span + chunk - 1) / chunk;
   hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), dim3(nchunk, a.nkv, a.B), dim3(64 * G), 0, s, a, part, nchunk,
                      chunk);
   hipError_t e = hipGetLastError();
@@ -652,8 +655,8 @@ size_t attn_prefill_part_bytes(int B, int S, int nkv, int G, int d, int NC) {
 }
 
 template <typename T>
-hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s) {
-  ZAYA_DISPATCH_DG(launch_decode_dg, a, part, maxlen, s);
+hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int span, hipStream_t s) {
+  ZAYA_DISPATCH_DG(launch_decode_dg, a, part, span, s);
 }
 
 size_t attn_decode_part_bytes(int B, int nkv, int G, int d) {

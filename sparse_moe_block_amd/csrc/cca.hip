@@ -19,6 +19,8 @@
 // time (two when d = 64). Lane p owns the dim pair (da, db) of every head of the group:
 // for p < rope_dim/2 that pair is the rotary pair, so the rotation never leaves the
 // lane; the head norms are reductions over the d/2 lanes of a token.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         const int t2 = base + sl;
         if (t2 >= t_end) continue;
         const u32x4 val = *reinterpret_cast<const u32x4*>(outs + ((wave * tpw + sl) * (G + 2) + rw) * d + ch * E16);
-        const size_t pos2 = (size_t)(L0 + t2);
+        const size_t pos2 = a.ring ? (size_t)((L0 + t2) % a.cap) : (size_t)(L0 + t2);  // cache slot
         T* dst;
         T* tap;
         if (rw < G) {
@@ -540,6 +542,39 @@ __global__ __launch_bounds__(256) void conv2_kernel(Conv2Args<T> a) {
 }
 
 size_t conv2_lds_bytes(int d, int act_bytes) { return (size_t)kC2Rows * (2 * d + 8) * act_bytes; }
+
+// ---- ring caches: the last positions of a fresh prefill, stored at slot p % cap
+template <typename T>
+__global__ __launch_bounds__(256) void ring_store_kernel(const T* __restrict__ Kw, const T* __restrict__ Vw,
+                                                         T* __restrict__ K, T* __restrict__ V, int S, int d,
+                                                         int cap, int n) {
+  // row i of the (sequence, KV head) pairs' kept positions; chunks of 16 bytes
+  constexpr int E16 = 16 / (int)sizeof(T);
+  const int cpr = d / E16, keep = min(S, cap), p0 = S - keep;
+  const long long total = 2LL * n * keep * cpr;
+  for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < total; q += (long long)gridDim.x * 256) {
+    const int cc = (int)(q % cpr);
+    const long long rest = q / cpr;
+    const int j = (int)(rest % keep), pair = (int)((rest / keep) % n), kv = (int)(rest / ((long long)keep * n));
+    const int p = p0 + j;
+    const T* src = (kv ? Vw : Kw) + ((size_t)pair * S + p) * d + cc * E16;
+    T* dst = (kv ? V : K) + ((size_t)pair * cap + p % cap) * d + cc * E16;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+template <typename T>
+hipError_t launch_ring_store(const T* Kw, const T* Vw, T* K, T* V, int B, int nkv, int S, int d, int cap,
+                             hipStream_t s) {
+  const long long total = 2LL * B * nkv * std::min(S, cap) * (d / (16 / (int)sizeof(T)));
+  const int grid = (int)std::min<long long>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL((ring_store_kernel<T>), dim3(grid), dim3(256), 0, s, Kw, Vw, K, V, S, d, cap, B * nkv);
+  return hipGetLastError();
+}
+template hipError_t launch_ring_store<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, bf16_t*, int, int, int, int, int,
+                                              hipStream_t);
+template hipError_t launch_ring_store<float>(const float*, const float*, float*, float*, int, int, int, int, int,
+                                             hipStream_t);
 
 // dynamic LDS the conv2 launches may ask for (fp32, d = 128 needs ~103 KB); the kernel's
 // static row tables come on top, within the CU's 160 KB

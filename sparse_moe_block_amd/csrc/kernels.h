@@ -53,9 +53,15 @@ struct CcaArgs {
   float theta;
   int conv_k = 3;         // 3: one depthwise conv; 2: depthwise k2 then grouped k2
   const T* y2 = nullptr;  // conv_k == 2: the convolved q/k channels [B*S][C] (launch_conv2)
+  int ring = 0;           // K/V slot of position p: p % cap (else p)
 };
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s);
+// Store the keys and values of positions max(0, S - cap) .. S-1 of fresh sequences,
+// formed in Kw/Vw [B, nkv, S, d], into ring caches K/V [B, nkv, cap, d] at slot p % cap.
+template <typename T>
+hipError_t launch_ring_store(const T* Kw, const T* Vw, T* K, T* V, int B, int nkv, int S, int d, int cap,
+                             hipStream_t s);
 
 // The printout's two-stage q/k convolution (conv_k == 2) of every token: depthwise
 // kernel 2 (conv_w [C][2], conv_b), then grouped kernel 2 with one group per head
@@ -88,13 +94,16 @@ struct AttnArgs {
   T* O;  // [B, S, nh, d]
   const int32_t* cache_len;  // device [B]
   int B, S, nh, nkv, d, cap, window;
+  int ring = 0;  // decode only: position p lives in slot p % cap
 };
 template <typename T>
 hipError_t launch_attn_prefill(const AttnArgs<T>& a, float* part, int NC, hipStream_t s);
 int attn_prefill_chunks(int S, int max_cache_len, int window);
 size_t attn_prefill_part_bytes(int B, int S, int nkv, int G, int d, int NC);
 template <typename T>
-hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int maxlen, hipStream_t s);
+// span: the largest number of positions from a sequence's 64-aligned window start (0
+// without a window) to its new token, over the batch
+hipError_t launch_attn_decode(const AttnArgs<T>& a, float* part, int span, hipStream_t s);
 size_t attn_decode_part_bytes(int B, int nkv, int G, int d);
 
 // ---- router MLP + selection (+ skip-token merge)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 #include <cstdarg>
 #include <cstdio>
@@ -159,6 +160,7 @@ template <typename T>
 int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, int S, bool decode, const float* x,
               const void* s_in, float* x_out, void* s_out, const zaya_cca_cache* cache, const zaya_taps* taps,
               char* ws, const Plan& p, int max_len, hipStream_t st) {
+  // max_len: prefill, the largest cache_len + S; decode, the attention span (see launch_attn_decode)
   const int H = c->hidden, nh = c->n_heads, nkv = c->n_kv_heads, d = c->head_dim, E = c->n_experts;
   const int I = c->expert_inter, R = c->router_hidden;
   const int T_ = B * S;
@@ -205,9 +207,13 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
     HIPCHK(launch_fill_i32((int32_t*)(ws + p.cache_len), B, 0, st));
     cl_dev = (const int32_t*)(ws + p.cache_len);
   }
-  T* Kc = cache ? (T*)cache->K : (T*)(ws + p.Kw);
-  T* Vc = cache ? (T*)cache->V : (T*)(ws + p.Vw);
-  const int cap = cache ? cache->cap : S;
+  // a ring cache takes fresh prefills (checked): their keys and values are formed in the
+  // workspace and the last positions stored afterwards; a decode step writes its slot
+  const bool ring_prefill = cache && cache->ring && !decode;
+  const int ring = cache && cache->ring && decode ? 1 : 0;
+  T* Kc = cache && !ring_prefill ? (T*)cache->K : (T*)(ws + p.Kw);
+  T* Vc = cache && !ring_prefill ? (T*)cache->V : (T*)(ws + p.Vw);
+  const int cap = cache && !ring_prefill ? cache->cap : S;
   T* conv_state = cache ? (T*)cache->conv_state : (T*)(ws + p.convw);
   T* prev_hs = cache ? (T*)cache->prev_hs : (T*)(ws + p.prevw);
 
@@ -233,11 +239,12 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   }
   CcaArgs<T> ca{P, QR, vdp, W(w->conv_w), W(w->conv_b), W(w->temp), conv_state, prev_hs, xn, cl_dev, Q, Kc, Vc, cap,
                 (T*)tp.attention_queries, (T*)tp.attention_keys, (T*)tp.attention_values,
-                B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta, c->conv_k, y2};
+                B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta, c->conv_k, y2, ring};
   HIPCHK(launch_cca<T>(ca, st));
+  if (ring_prefill) HIPCHK(launch_ring_store<T>(Kc, Vc, (T*)cache->K, (T*)cache->V, B, nkv, S, d, cache->cap, st));
   // a4: attention
   HIPCHK(mark(3));
-  AttnArgs<T> aa{Q, Kc, Vc, O, cl_dev, B, S, nh, nkv, d, cap, c->sliding_window};
+  AttnArgs<T> aa{Q, Kc, Vc, O, cl_dev, B, S, nh, nkv, d, cap, c->sliding_window, ring};
   if (decode)
     HIPCHK(launch_attn_decode<T>(aa, (float*)(ws + p.part), max_len, st));
   else
@@ -301,6 +308,38 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
 
 size_t block_ws_bytes(const zaya_block_config* c, int B, int S, int decode) { return plan_block(c, B, S, decode).total; }
 
+// Cache checks of one block call. *max_len: prefill, the largest cache_len + S; decode,
+// the largest span from a sequence's 64-aligned window start to its new token.
+int check_cache(const zaya_block_config* c, const zaya_cca_cache* cache, int B, int S, bool decode, int* max_len) {
+  *max_len = S;
+  if (!cache) return ZAYA_OK;
+  if (!cache->K || !cache->V || !cache->conv_state || !cache->prev_hs || !cache->cache_len)
+    return fail(ZAYA_EINVAL, "cache has a NULL member");
+  if (cache->cap <= 0) return fail(ZAYA_ECACHE, "cache cap %d", cache->cap);
+  const int W = c->sliding_window;
+  if (cache->ring) {
+    if (W < 0) return fail(ZAYA_ECACHE, "a ring cache needs a sliding window");
+    if (cache->cap < W + 1) return fail(ZAYA_ECACHE, "ring cache cap %d < sliding_window + 1 = %d", cache->cap, W + 1);
+  }
+  int span = 1;
+  for (int b = 0; b < B; ++b) {
+    const int L0 = cache->cache_len[b];
+    if (L0 < 0) return fail(ZAYA_ECACHE, "cache_len[%d] = %d", b, L0);
+    if (cache->ring) {
+      if (!decode && L0 != 0)
+        return fail(ZAYA_ECACHE, "prefill into a ring cache needs fresh sequences (cache_len[%d] = %d)", b, L0);
+      if (L0 > INT_MAX - S) return fail(ZAYA_ECACHE, "cache_len[%d] = %d too large", b, L0);
+    } else if ((long long)L0 + S > cache->cap) {
+      return fail(ZAYA_ECACHE, "cache_len[%d] = %d with S = %d exceeds cap %d", b, L0, S, cache->cap);
+    }
+    *max_len = std::max(*max_len, L0 + S);
+    const int kbase = W >= 0 ? (std::max(0, L0 - W) / 64) * 64 : 0;
+    span = std::max(span, L0 + 1 - kbase);
+  }
+  if (decode) *max_len = span;
+  return ZAYA_OK;
+}
+
 int block_entry(const zaya_block_config* c, const zaya_block_weights* w, int B, int S, bool decode, const float* x,
                 const void* s_in, float* x_out, void* s_out, const zaya_cca_cache* cache, const zaya_taps* taps,
                 void* ws, size_t ws_bytes, void* stream) {
@@ -318,17 +357,7 @@ int block_entry(const zaya_block_config* c, const zaya_block_weights* w, int B, 
   if (overlap(s_in, T_ * c->router_hidden * A, s_out, T_ * c->router_hidden * A))
     return fail(ZAYA_EALIAS, "router_state_out aliases router_state_in");
   int max_len = S;
-  if (cache) {
-    if (!cache->K || !cache->V || !cache->conv_state || !cache->prev_hs || !cache->cache_len)
-      return fail(ZAYA_EINVAL, "cache has a NULL member");
-    if (cache->cap <= 0) return fail(ZAYA_ECACHE, "cache cap %d", cache->cap);
-    for (int b = 0; b < B; ++b) {
-      const int L0 = cache->cache_len[b];
-      if (L0 < 0 || (long long)L0 + S > cache->cap)
-        return fail(ZAYA_ECACHE, "cache_len[%d] = %d with S = %d exceeds cap %d", b, L0, S, cache->cap);
-      max_len = std::max(max_len, L0 + S);
-    }
-  }
+  if ((rc = check_cache(c, cache, B, S, decode, &max_len))) return rc;
   const size_t need = block_ws_bytes(c, B, S, decode);
   if (!ws || ws_bytes < need) return fail(ZAYA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (((uintptr_t)ws) & 255) return fail(ZAYA_EWORKSPACE, "workspace not 256-byte aligned");
@@ -339,10 +368,18 @@ int block_entry(const zaya_block_config* c, const zaya_block_weights* w, int B, 
   return run_block<float>(c, w, B, S, decode, x, s_in, x_out, s_out, cache, taps, (char*)ws, p, max_len, st);
 }
 
+// Block l's configuration in a stack: with window_layers 1 (2) only the even (odd)
+// blocks keep block.sliding_window, the others attend to the whole prefix.
+zaya_block_config layer_config(const zaya_stack_config* s, int l) {
+  zaya_block_config c = s->block;
+  if ((s->window_layers == 1 && (l & 1)) || (s->window_layers == 2 && !(l & 1))) c.sliding_window = -1;
+  return c;
+}
+
 // Stack workspace: the block workspace, then two fp32 streams, two router states and
 // the final normed stream.
 struct StackPlan {
-  size_t block, x0, x1, s0, s1, xf, total;
+  size_t block, block_bytes, x0, x1, s0, s1, xf, total;
 };
 
 StackPlan plan_stack(const zaya_stack_config* c, int B, int S) {
@@ -350,7 +387,10 @@ StackPlan plan_stack(const zaya_stack_config* c, int B, int S) {
   const size_t T_ = (size_t)B * S;
   const size_t A = act_bytes(&c->block);
   p.block = 0;
-  size_t o = align256(block_ws_bytes(&c->block, B, S, 0));
+  // the largest block workspace over the layers' configurations (windowed or not)
+  const zaya_block_config l0 = layer_config(c, 0), l1 = layer_config(c, 1);
+  p.block_bytes = std::max(block_ws_bytes(&l0, B, S, 0), block_ws_bytes(&l1, B, S, 0));
+  size_t o = align256(p.block_bytes);
   auto take = [&](size_t bytes) {
     size_t at = o;
     o += align256(bytes);
@@ -389,7 +429,8 @@ int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w,
 }
 
 size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S) {
-  if (!cfg || check_config(&cfg->block) || B <= 0 || S <= 0) return 0;
+  if (!cfg || check_config(&cfg->block) || B <= 0 || S <= 0 || cfg->window_layers < 0 || cfg->window_layers > 2)
+    return 0;
   return plan_stack(cfg, B, S).total;
 }
 
@@ -407,15 +448,13 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
     if ((rc = check_weights(&cfg->block, &w->blocks[l]))) return fail(rc, "block %d: %s", l, g_err.c_str());
   if (B <= 0 || S <= 0) return fail(ZAYA_EINVAL, "B=%d S=%d must be positive", B, S);
   if (!ids || !logits) return fail(ZAYA_EINVAL, "ids and logits are required");
+  if (cfg->window_layers < 0 || cfg->window_layers > 2)
+    return fail(ZAYA_ESHAPE, "window_layers %d not in {0, 1, 2}", cfg->window_layers);
   if (caches) {
     for (int l = 0; l < cfg->n_layers; ++l) {
-      const zaya_cca_cache& cc = caches[l];
-      if (!cc.K || !cc.V || !cc.conv_state || !cc.prev_hs || !cc.cache_len)
-        return fail(ZAYA_EINVAL, "cache of block %d has a NULL member", l);
-      for (int b = 0; b < B; ++b)
-        if (cc.cache_len[b] < 0 || (long long)cc.cache_len[b] + S > cc.cap)
-          return fail(ZAYA_ECACHE, "block %d: cache_len[%d] = %d with S = %d exceeds cap %d", l, b, cc.cache_len[b],
-                      S, cc.cap);
+      const zaya_block_config lc = layer_config(cfg, l);
+      int ml;
+      if ((rc = check_cache(&lc, &caches[l], B, S, false, &ml))) return fail(rc, "block %d: %s", l, g_err.c_str());
     }
   }
   StackPlan p = plan_stack(cfg, B, S);
@@ -434,13 +473,14 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
                     : launch_embed<float>(ids, (const float*)w->embed, (const float*)w->emb_shift,
                                           (const float*)w->emb_scale, xs[0], nullptr, T_, H, cfg->vocab, st);
   if (e != hipSuccess) return fail(ZAYA_EHIP, "embed: %s", hipGetErrorString(e));
-  const size_t bws = block_ws_bytes(c, B, S, 0);
+  const size_t bws = p.block_bytes;
   const void* s_in = nullptr;
   int cur = 0;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const zaya_cca_cache* cc = caches ? &caches[l] : nullptr;
     const zaya_taps* tt = taps ? &taps[l] : nullptr;
-    rc = block_entry(c, &w->blocks[l], B, S, false, xs[cur], s_in, xs[cur ^ 1], ss[cur], cc, tt, ws, bws, stream);
+    const zaya_block_config lc = layer_config(cfg, l);
+    rc = block_entry(&lc, &w->blocks[l], B, S, false, xs[cur], s_in, xs[cur ^ 1], ss[cur], cc, tt, ws, bws, stream);
     if (rc) return fail(rc, "block %d: %s", l, g_err.c_str());
     s_in = ss[cur];
     cur ^= 1;

@@ -203,6 +203,32 @@ def test_cache_bounds_are_checked(L):
     assert rc == -4
 
 
+def test_ring_cache_validation(L):
+    bw = Z.BlockWeights(*([FAKE] * len(Z.WEIGHT_FIELDS)))
+    lens = (C.c_int32 * 3)(500, 7, 0)  # a ring may hold sequences longer than its cap
+
+    def decode(cfg, cap, ring=1):
+        cache = Z.CcaCache(FAKE, FAKE + (5 << 32), cap, FAKE + (6 << 32), FAKE + (7 << 32),
+                           C.cast(lens, C.POINTER(C.c_int32)), None, ring)
+        return L.zaya_block_decode(C.byref(Z.block_config(cfg)), C.byref(bw), 3, FAKE, FAKE + (1 << 32),
+                                   FAKE + (2 << 32), FAKE + (3 << 32), C.byref(cache), None, FAKE + (4 << 32), 0,
+                                   None)
+
+    win = CONFIGS["decode"].replace(sliding_window=100)
+    assert decode(win, 101) == -4  # valid: stops at the empty workspace
+    assert decode(win, 101, ring=0) == -5  # the same lengths overflow a linear cache
+    assert decode(CONFIGS["decode"], 101) == -5 and "window" in L.zaya_last_error().decode()
+    assert decode(win, 100) == -5 and "cap" in L.zaya_last_error().decode()
+    # prefill into a ring: fresh sequences only
+    cache = Z.CcaCache(FAKE, FAKE + (5 << 32), 101, FAKE + (6 << 32), FAKE + (7 << 32),
+                       C.cast(lens, C.POINTER(C.c_int32)), None, 1)
+    rc = _prefill(L, _args(win.replace(batch=3, seq=16, decode=False), 3, 16, cache=C.byref(cache), ws_bytes=0))
+    assert rc == -5 and "fresh" in L.zaya_last_error().decode()
+    lens[0] = lens[1] = 0
+    assert _prefill(L, _args(win.replace(batch=3, seq=16, decode=False), 3, 16, cache=C.byref(cache),
+                             ws_bytes=0)) == -4
+
+
 def test_stack_validation(L):
     cfg = CONFIGS["stack"]
     bw = (Z.BlockWeights * cfg.num_layers)(*[Z.BlockWeights(*([FAKE] * len(Z.WEIGHT_FIELDS)))
@@ -220,6 +246,15 @@ def test_stack_validation(L):
     assert call(sc) == -4  # everything else valid: the empty workspace is what stops it
     bad = Z.StackConfig(Z.block_config(cfg.replace(head_dim=80)), cfg.num_layers, cfg.vocab_size)
     assert call(bad) == -2
+    # hybrid stacks: window_layers in {0, 1, 2}
+    assert call(Z.StackConfig(Z.block_config(cfg.replace(sliding_window=64)), cfg.num_layers, cfg.vocab_size, 1)) == -4
+    bad = Z.StackConfig(Z.block_config(cfg), cfg.num_layers, cfg.vocab_size, 3)
+    assert call(bad) == -2 and "window_layers" in L.zaya_last_error().decode()
+    assert Z.zaya_stack_workspace_bytes(cfg.replace(window_layers=3), 4, 16) == 0
+    # the workspace covers the windowed and the full-attention blocks
+    hyb = cfg.replace(sliding_window=64, window_layers=1)
+    assert Z.zaya_stack_workspace_bytes(hyb, 4, 2048) >= max(
+        Z.zaya_stack_workspace_bytes(cfg, 4, 2048), Z.zaya_stack_workspace_bytes(cfg.replace(sliding_window=64), 4, 2048))
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

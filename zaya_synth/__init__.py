@@ -48,6 +48,7 @@ class ZayaConfig:
     conv_k: int = 3  # 3: one depthwise kernel-3 conv; 2: the printout's depthwise k2 then grouped k2
     rms_norm_eps: float = 1e-5
     sliding_window: int = -1  # < 0: off; else key visible iff p_q - p_k <= window
+    window_layers: int = 0  # stacks: 0 all blocks windowed, 1 blocks 0, 2, ..., 2 blocks 1, 3, ...
     kv_len: int = 0  # tokens already in the cache before this call
     decode: bool = False
     num_layers: int = 1
