@@ -181,7 +181,7 @@ __device__ __forceinline__ QTile qtile(int qblk, int S, int L0, int W, int NC) {
   const int klo = W >= 0 ? max(0, r.qp_min - W) : 0;
   r.kt_begin = klo / 64;
   r.n = r.qp_max / 64 + 1 - r.kt_begin;
-  r.nc = min(NC, r.n);
+  r.nc = min(NC, r.n);  // short ranges split too: their small units fill the last round
   return r;
 }
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int c = blockIdx.x % NC;
   const int qblk = nqb - 1 - (int)(blockIdx.x / NC);
   const int g = blockIdx.y, b = blockIdx.z;
-  const int S = a.S, L0 = a.cache_len[b];
+  const int S = a.S, L0 = cached_len(a.cache_len, b);
   const int W = a.window;
   const QTile qt = qtile(qblk, S, L0, W, NC);
   if (c >= qt.nc) return;
@@ -375,55 +375,62 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // Merge the chunks of every split query tile: O = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
-// One wave per head; lane pair (2r, 2r+1) owns row r, each lane half of its dims, so
-// every load of the pass is independent of the others.
+// One thread per (query row, head, 4 dims): kRowsPerWg rows of a tile per workgroup,
+// so the pass reads the partials with many independent 16-byte loads in flight.
+template <int D, int G>
+struct CombineShape {
+  static constexpr int kNJ = D / 4;                                      // 4-dim groups per row
+  static constexpr int kRowsPerWg = 256 / (G * kNJ) > 0 ? 256 / (G * kNJ) : 1;
+  static constexpr int kThreads = kRowsPerWg * G * kNJ;
+};
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * G) void attn_prefill_combine_kernel(AttnArgs<T> a, const float* __restrict__ part,
-                                                                       int NC) {
+__global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a, const float* __restrict__ part,
+                                                                   int NC) {
+  using CS = CombineShape<D, G>;
   const int nqb = (a.S + 31) / 32;
-  const int qblk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int L0 = a.cache_len[b];
+  const int qblk = blockIdx.x / (32 / CS::kRowsPerWg), g = blockIdx.y, b = blockIdx.z;
+  const int L0 = cached_len(a.cache_len, b);
   const QTile qt = qtile(qblk, a.S, L0, a.window, NC);
   if (qt.nc == 1) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = g * G + wave;
-  const int row = lane >> 1, half = lane & 1;
+  const int j = threadIdx.x % CS::kNJ, wave = (threadIdx.x / CS::kNJ) % G;
+  const int row = (blockIdx.x % (32 / CS::kRowsPerWg)) * CS::kRowsPerWg + threadIdx.x / (CS::kNJ * G);
   if (row >= qt.nq) return;
+  const int h = g * G + wave;
   const size_t unit0 = (((size_t)b * a.nkv + g) * nqb + qblk) * NC;
   const size_t ustride = (size_t)G * 32 * (D + 2);
   const float* base = part + (unit0 * G + wave) * 32 * (D + 2) + (size_t)row * (D + 2);
-  float mc[16];
+  // chunks in groups of four, loads issued together (past the last chunk they re-read it)
   float M = -INFINITY;
+  for (int c0 = 0; c0 < qt.nc; c0 += 4) {
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
-    mc[cc] = cc < qt.nc ? base[cc * ustride + D] : -INFINITY;
-    M = fmaxf(M, mc[cc]);
+    for (int cc = 0; cc < 4; ++cc) M = fmaxf(M, base[min(c0 + cc, qt.nc - 1) * ustride + D]);
   }
-  float lsum = 0.f;
-  float acc[D / 2];
+  float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < qt.nc; c0 += 4) {
+    float mc[4], lc[4];
+    float4 v[4];
 #pragma unroll
-  for (int j = 0; j < D / 2; ++j) acc[j] = 0.f;
+    for (int cc = 0; cc < 4; ++cc) {
+      const int ci = min(c0 + cc, qt.nc - 1);
+      mc[cc] = base[ci * ustride + D];
+      lc[cc] = base[ci * ustride + D + 1];
+      v[cc] = *reinterpret_cast<const float4*>(base + ci * ustride + 4 * j);
+    }
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
-    if (cc >= qt.nc) break;
-    const float sc = mc[cc] == -INFINITY ? 0.f : exp2f(mc[cc] - M);
-    const float* pr = base + cc * ustride + half * (D / 2);
-    lsum += sc * base[cc * ustride + D + 1];
-#pragma unroll
-    for (int j = 0; j < D / 2; j += 4) {
-      float v[4];
-      load4(pr + j, v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j + i] += sc * v[i];
+    for (int cc = 0; cc < 4; ++cc) {
+      const float sc = (c0 + cc >= qt.nc || mc[cc] == -INFINITY) ? 0.f : exp2f(mc[cc] - M);
+      lsum += sc * lc[cc];
+      acc[0] += sc * v[cc].x;
+      acc[1] += sc * v[cc].y;
+      acc[2] += sc * v[cc].z;
+      acc[3] += sc * v[cc].w;
     }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  T* orow = a.O + (((size_t)b * a.S + qt.q0 + row) * a.nh + h) * D + half * (D / 2);
-#pragma unroll
-  for (int j = 0; j < D / 2; j += 4) {
-    float v[4] = {acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv};
-    store4(orow + j, v);
-  }
+  T* orow = a.O + (((size_t)b * a.S + qt.q0 + row) * a.nh + h) * D + 4 * j;
+  float o4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  store4(orow, o4);
 }
 
 // ----------------------------------------------------------------------------- decode
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = g * G + wave;
-  const int L0 = a.cache_len[b];
+  const int L0 = cached_len(a.cache_len, b);
   const int qp = L0;  // the new token's position
   const int kvalid = L0 + 1;
   const int W = a.window;
@@ -599,7 +606,9 @@ static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, h
   hipLaunchKernelGGL((attn_prefill_kernel<T, D, G>), dim3(nqb * NC, a.nkv, a.B), dim3(64 * G), 0, s, a, part, NC);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || NC == 1) return e;
-  hipLaunchKernelGGL((attn_prefill_combine_kernel<T, D, G>), dim3(nqb, a.nkv, a.B), dim3(64 * G), 0, s, a, part, NC);
+  using CS = CombineShape<D, G>;
+  hipLaunchKernelGGL((attn_prefill_combine_kernel<T, D, G>), dim3(nqb * (32 / CS::kRowsPerWg), a.nkv, a.B),
+                     dim3(CS::kThreads), 0, s, a, part, NC);
   return hipGetLastError();
 }
 

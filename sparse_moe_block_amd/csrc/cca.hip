@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   T* y2s = outs + 4 * (128 / d) * (G + 2) * d;
   const int S = a.S, QR = a.qkv_ld;
   const int kcol = nh * d, vccol = nh * d + nkv * d, vdcol = vccol + nkv * d / 2;
-  const int L0 = a.cache_len[b];
+  const int L0 = cached_len(a.cache_len, b);
   const bool fresh = L0 == 0;
   const int t0 = tile * kCcaTokens;
   const int t_end = min(S, t0 + kCcaTokens);
@@ -106,12 +106,13 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       u32x4 val[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        const int ch = c0 + k * nthr;
-        const int rr = ch / per_row, t = t0 - 2 + rr;
+        // indices clamped into range so no load sits behind a branch (rows before the
+        // sequence start are the history, written below; chunks past the tile unused)
+        const int ch = min(c0 + k * nthr, nrows * per_row - 1);
+        const int rr = ch / per_row, t = max(t0 - 2 + rr, 0);
         int src, dst;
         chunk_cols(ch % per_row, src, dst);
-        if (ch < nrows * per_row && t >= 0)  // rows before the sequence start are the history
-          val[k] = *reinterpret_cast<const u32x4*>(a.P + ((size_t)b * S + t) * QR + src);
+        val[k] = *reinterpret_cast<const u32x4*>(a.P + ((size_t)b * S + t) * QR + src);
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
@@ -129,9 +130,9 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         u32x4 val[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-          const int ch = c0 + k * nthr, cc = ch % per_y;
+          const int ch = min(c0 + k * nthr, ny - 1), cc = ch % per_y;
           const int src = cc < segq ? g * G * d + cc * E16 : kcol + g * d + (cc - segq) * E16;
-          if (ch < ny) val[k] = *reinterpret_cast<const u32x4*>(a.y2 + ((size_t)b * S + t0 + ch / per_y) * a.C + src);
+          val[k] = *reinterpret_cast<const u32x4*>(a.y2 + ((size_t)b * S + t0 + ch / per_y) * a.C + src);
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(256) void conv2_kernel(Conv2Args<T> a) {
   b1.load(a.conv_b + h * d + c);
   int cl[RPG];
 #pragma unroll
-  for (int j = 0; j < RPG; ++j) cl[j] = a.cache_len[min(r0 + m0 + j, rows - 1) / S];
+  for (int j = 0; j < RPG; ++j) cl[j] = cached_len(a.cache_len, min(r0 + m0 + j, rows - 1) / S);
 
   // z rows of this thread (rows past the tile are zero)
   Pack8<T> prev, cur;

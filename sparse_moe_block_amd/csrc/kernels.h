@@ -92,7 +92,7 @@ struct AttnArgs {
   const T* K;  // [B, nkv, cap, d]
   const T* V;
   T* O;  // [B, S, nh, d]
-  const int32_t* cache_len;  // device [B]
+  const int32_t* cache_len;  // device [B], or null: every sequence fresh
   int B, S, nh, nkv, d, cap, window;
   int ring = 0;  // decode only: position p lives in slot p % cap
 };

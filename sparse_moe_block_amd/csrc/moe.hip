@@ -98,8 +98,82 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict_
   }
 }
 
+// Up to kBucketPer * 1024 tokens in one sweep: every thread keeps its classes in
+// registers; per (chunk, wave, expert) counts come from ballots, one wave per expert
+// scans them into that expert's running prefix in (chunk, wave) order, and each token's
+// slot is its expert's offset + the prefix of its (chunk, wave) + its rank in the wave.
+// Three barriers in all.
+__global__ __launch_bounds__(1024) void bucket_small_kernel(const int32_t* __restrict__ cls, int ntok, int E,
+                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ ids) {
+  __shared__ int wpre[kBucketPer][16][32];  // counts, then exclusive prefixes within an expert
+  __shared__ int base[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int nch = (ntok + 1023) / 1024;
+  int c[kBucketPer], rank[kBucketPer];
+#pragma unroll
+  for (int j = 0; j < kBucketPer; ++j) {
+    const int t = j * 1024 + tid;
+    c[j] = t < ntok ? cls[max(min(t, ntok - 1), 0)] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kBucketPer; ++j) {
+    if (j >= nch) break;
+    int mine = 0;
+    rank[j] = 0;
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot(c[j] == e);
+      if (lane == e) mine = __popcll(m);
+      if (c[j] == e) rank[j] = __popcll(m & lt);
+    }
+    if (lane < E) wpre[j][wave][lane] = mine;
+  }
+  __syncthreads();
+  // wave w scans the (chunk, wave) counts of experts w, w + 16 (two entries per lane)
+  for (int e = wave; e < E; e += 16) {
+    const int n = nch * 16, k0 = 2 * lane;
+    const int v0 = k0 < n ? wpre[k0 >> 4][k0 & 15][e] : 0;
+    const int v1 = k0 + 1 < n ? wpre[(k0 + 1) >> 4][(k0 + 1) & 15][e] : 0;
+    int incl = v0 + v1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int excl = incl - v0 - v1;
+    if (k0 < n) wpre[k0 >> 4][k0 & 15][e] = excl;
+    if (k0 + 1 < n) wpre[(k0 + 1) >> 4][(k0 + 1) & 15][e] = excl + v0;
+    const int total = __shfl(incl, 63, 64);
+    if (lane == 0) base[e] = total;
+  }
+  __syncthreads();
+  if (wave == 0) {  // expert offsets: exclusive scan of the counts
+    const int n = lane < E ? base[lane] : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane < E) {
+      base[lane] = incl - n;
+      offsets[lane] = incl - n;
+    }
+    if (lane == E - 1) offsets[E] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kBucketPer; ++j) {
+    if (j >= nch) break;
+    if (c[j] >= 0 && c[j] < E) ids[base[c[j]] + wpre[j][wave][c[j]] + rank[j]] = j * 1024 + tid;
+  }
+}
+
 hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, int32_t* ids, hipStream_t s) {
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, cls, ntok, E, offsets, ids);
+  if (ntok <= kBucketPer * 1024 && E <= 32)
+    hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(1024), 0, s, cls, ntok, E, offsets, ids);
+  else
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, cls, ntok, E, offsets, ids);
   return hipGetLastError();
 }
 
@@ -254,7 +328,7 @@ template <typename T>
 hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
   if (a.ntok <= 32 * a.E) return launch_down_cfg<T, 16, 1, 4>(a, s);
-  return launch_down_cfg<T, 64, 2, 2>(a, s);
+  return launch_down_cfg<T, 128, 2, 2>(a, s);
 }
 
 // ----------------------------------------------------------------------------- FP8 experts

@@ -204,8 +204,7 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
       cl_dev = (const int32_t*)(ws + p.cache_len);
     }
   } else {
-    HIPCHK(launch_fill_i32((int32_t*)(ws + p.cache_len), B, 0, st));
-    cl_dev = (const int32_t*)(ws + p.cache_len);
+    cl_dev = nullptr;  // the kernels read a null table as all sequences fresh
   }
   // a ring cache takes fresh prefills (checked): their keys and values are formed in the
   // workspace and the last positions stored afterwards; a decode step writes its slot
