@@ -449,6 +449,11 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   __shared__ __attribute__((aligned(16))) char vt_s[64 * VROW];
   __shared__ __attribute__((aligned(16))) float q_s[G][D];
   __shared__ __attribute__((aligned(16))) float p_s[G][64];
+  // bf16: the query as stored and the probabilities rounded to bf16, for the
+  // v_dot2_f32_bf16 products (each multiplies two bf16 pairs exactly, sums in fp32)
+  constexpr bool kDot2 = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) uint32_t q2_s[G][D / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t p2_s[G][32];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -463,7 +468,12 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   const int c_lo = max(klo, kbase + c * chunk), c_hi = min(kvalid, kbase + (c + 1) * chunk);
   const float sscale = kLog2e / sqrtf((float)D);
 
-  for (int i = lane; i < D; i += 64) q_s[wave][i] = Act<T>::tof(a.Q[((size_t)b * a.nh + h) * D + i]);
+  if constexpr (kDot2) {
+    const uint32_t* qg = reinterpret_cast<const uint32_t*>(a.Q + ((size_t)b * a.nh + h) * D);
+    for (int i = lane; i < D / 2; i += 64) q2_s[wave][i] = qg[i];
+  } else {
+    for (int i = lane; i < D; i += 64) q_s[wave][i] = Act<T>::tof(a.Q[((size_t)b * a.nh + h) * D + i]);
+  }
 
   float m_run = -INFINITY, l_run = 0.f;
   float o[DPL];
@@ -507,15 +517,27 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
     const int kp = t0 + lane;
     const T* krow = reinterpret_cast<const T*>(kt_s + lane * KROW);
     float acc0 = 0.f, acc1 = 0.f;
+    if constexpr (kDot2) {
 #pragma unroll
-    for (int i = 0; i < D; i += 8) {
-      float kv[8];
-      load4(krow + i, kv);
-      load4(krow + i + 4, kv + 4);
-      const float4 qa = *reinterpret_cast<const float4*>(&q_s[wave][i]);
-      const float4 qb = *reinterpret_cast<const float4*>(&q_s[wave][i + 4]);
-      acc0 += qa.x * kv[0] + qa.y * kv[1] + qa.z * kv[2] + qa.w * kv[3];
-      acc1 += qb.x * kv[4] + qb.y * kv[5] + qb.z * kv[6] + qb.w * kv[7];
+      for (int i = 0; i < D; i += 8) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + i);
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(&q2_s[wave][i / 2]);
+        acc0 = dot2_bf16(kv[0], qv[0], acc0);
+        acc1 = dot2_bf16(kv[1], qv[1], acc1);
+        acc0 = dot2_bf16(kv[2], qv[2], acc0);
+        acc1 = dot2_bf16(kv[3], qv[3], acc1);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < D; i += 8) {
+        float kv[8];
+        load4(krow + i, kv);
+        load4(krow + i + 4, kv + 4);
+        const float4 qa = *reinterpret_cast<const float4*>(&q_s[wave][i]);
+        const float4 qb = *reinterpret_cast<const float4*>(&q_s[wave][i + 4]);
+        acc0 += qa.x * kv[0] + qa.y * kv[1] + qa.z * kv[2] + qa.w * kv[3];
+        acc1 += qb.x * kv[4] + qb.y * kv[5] + qb.z * kv[6] + qb.w * kv[7];
+      }
     }
     const bool vis = kp >= c_lo && kp < c_hi;
     const float sv = vis ? (acc0 + acc1) * sscale : -INFINITY;
@@ -526,22 +548,44 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
     const float pv = __builtin_amdgcn_exp2f(sv - m_use);
     l_run = l_run * alpha + pv;
     m_run = m_new;
-    p_s[wave][lane] = pv;
+    if constexpr (kDot2) {
+      // key pairs (2m, 2m+1): the lane of key 2m packs both probabilities
+      const float pnext = __shfl_down(pv, 1, 64);
+      if (!(lane & 1)) p2_s[wave][lane >> 1] = pack_bf16x2(pv, pnext);
+    } else {
+      p_s[wave][lane] = pv;
+    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int j = 0; j < DPL; ++j) o[j] *= alpha;
-    // weighted sum: lane owns dims [lane*DPL, lane*DPL + DPL); four keys per step
+    // weighted sum: lane owns dims [lane*DPL, lane*DPL + DPL)
+    if constexpr (kDot2 && DPL == 2) {
+      // two keys per product: (v_k[d], v_k+1[d]) pairs built with one byte permute each
 #pragma unroll 4
-    for (int k = 0; k < 64; k += 4) {
-      const float4 pk = *reinterpret_cast<const float4*>(&p_s[wave][k]);
-      const float pkk[4] = {pk.x, pk.y, pk.z, pk.w};
+      for (int k = 0; k < 64; k += 8) {
+        const u32x4 pp = *reinterpret_cast<const u32x4*>(&p2_s[wave][k / 2]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const T* vrow = reinterpret_cast<const T*>(vt_s + (k + kk) * VROW) + lane * DPL;
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t v0 = *reinterpret_cast<const uint32_t*>(vt_s + (k + 2 * kk) * VROW + lane * 4);
+          const uint32_t v1 = *reinterpret_cast<const uint32_t*>(vt_s + (k + 2 * kk + 1) * VROW + lane * 4);
+          o[0] = dot2_bf16(pp[kk], __builtin_amdgcn_perm(v1, v0, 0x05040100u), o[0]);  // low halves: dim 2 lane
+          o[1] = dot2_bf16(pp[kk], __builtin_amdgcn_perm(v1, v0, 0x07060302u), o[1]);  // high halves
+        }
+      }
+    } else {
+      // four keys per step
+#pragma unroll 4
+      for (int k = 0; k < 64; k += 4) {
+        const float4 pk = *reinterpret_cast<const float4*>(&p_s[wave][k]);
+        const float pkk[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) o[j] += pkk[kk] * Act<T>::tof(vrow[j]);
+        for (int kk = 0; kk < 4; ++kk) {
+          const T* vrow = reinterpret_cast<const T*>(vt_s + (k + kk) * VROW) + lane * DPL;
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) o[j] += pkk[kk] * Act<T>::tof(vrow[j]);
+        }
       }
     }
   }

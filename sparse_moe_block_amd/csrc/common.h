@@ -30,6 +30,13 @@ __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint3
 // against the bit-level rounding rule on all 2^32 inputs, denormals and NaNs included.
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
+// acc + a.lo*b.lo + a.hi*b.hi for two packed bf16 pairs (v_dot2_f32_bf16: the products
+// are exact in fp32, the sum accumulates in fp32).
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), acc, false);
+}
+
 // Cached tokens of sequence b: a null table means every sequence is fresh.
 __device__ __forceinline__ int cached_len(const int32_t* cache_len, int b) { return cache_len ? cache_len[b] : 0; }
 
