@@ -216,15 +216,17 @@ static inline int moe_grid(int ntok, int E, int BM, int ntn) {
   return 8 * ((nmax + 7) / 8);
 }
 
-template <typename T, int BM, int WM, int WN>
+// BN weight rows per item = BN/2 activation columns, gate and up in alternating 16-row
+// blocks.
+template <typename T, int BM, int WM, int WN, int BN = 128>
 __global__ __launch_bounds__(WM* WN * 64)
-__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
-  constexpr int BN = 128;  // 64 activation columns: gate and up in alternating 16-row blocks
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
+  constexpr int CN = BN / 2;  // activation columns per item
   using Tile = GemmTile<T, BM, BN, WM, WN>;
   static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
-  int e, r0, n_e, j;  // j: activation columns [64j, 64j + 64)
-  if (!moe_item(a.offsets, a.E, BM, a.I / 64, e, r0, n_e, j)) return;
+  int e, r0, n_e, j;  // j: activation columns [CN j, CN j + CN)
+  if (!moe_item(a.offsets, a.E, BM, a.I / CN, e, r0, n_e, j)) return;
   const int base = a.offsets[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
@@ -232,7 +234,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) 
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
   t.set_b([&](int r) -> const T* {
     const int blk = r >> 4, w16 = r & 15;
-    const int row = ((blk & 1) ? a.I : 0) + 64 * j + (blk >> 1) * 16 + w16;
+    const int row = ((blk & 1) ? a.I : 0) + CN * j + (blk >> 1) * 16 + w16;
     return Wg + (size_t)row * a.H;
   });
   t.run(smem, a.H / Tile::kBK);
@@ -246,7 +248,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) 
     T* nrow = a.neurons + (size_t)(base + m) * a.I;
 #pragma unroll
     for (int pp = 0; pp < Tile::kTN / 2; ++pp) {
-      const int col = 64 * j + (wn * (Tile::kTN / 2) + pp) * 16 + (lane >> 4) * 4;
+      const int col = CN * j + (wn * (Tile::kTN / 2) + pp) * 16 + (lane >> 4) * 4;
       float v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -260,10 +262,9 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) 
   }
 }
 
-template <typename T, int BM, int WM, int WN>
+template <typename T, int BM, int WM, int WN, int BN = 128>
 __global__ __launch_bounds__(WM* WN * 64)
-__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
-  constexpr int BN = 128;
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
   using Tile = GemmTile<T, BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
   int e, r0, n_e, c;
@@ -300,16 +301,16 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, 128, WM, WN>::kWavesPerEU))) 
   });
 }
 
-template <typename T, int BM, int WM, int WN>
+template <typename T, int BM, int WM, int WN, int BN = 128>
 static hipError_t launch_gateup_cfg(const MoeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN>), dim3(moe_grid(a.ntok, a.E, BM, a.I / 64)),
+  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN, BN>), dim3(moe_grid(a.ntok, a.E, BM, a.I / (BN / 2))),
                      dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int BM, int WM, int WN>
+template <typename T, int BM, int WM, int WN, int BN = 128>
 static hipError_t launch_down_cfg(const MoeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN>), dim3(moe_grid(a.ntok, a.E, BM, a.H / 128)),
+  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN, BN>), dim3(moe_grid(a.ntok, a.E, BM, a.H / BN)),
                      dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
