@@ -97,25 +97,41 @@ static hipError_t launch_cfg(const T* A, int lda, const T* B, int ldb, int M, in
 
 // Split-K for GEMMs with few rows (decode): each workgroup reduces one K range of a
 // 64 x 64 output tile into fp32 partials; a second pass sums the ranges in a fixed
-// order and applies the epilogue, so results do not depend on scheduling.
+// order and applies the epilogue, so results do not depend on scheduling. One launch
+// may carry two problems with the same K (their tiles one after the other).
 template <typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_splitk_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
-                                                          int ldb, int M, int N, int K, int kparts,
-                                                          float* __restrict__ part) {
+struct SplitProb {
+  const T* A;
+  int lda;
+  const T* B;
+  int ldb;
+  int M, N;
+  float* part;  // [kparts][M][N]
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_splitk_kernel(SplitProb<T> p1,
+                                                                                                  SplitProb<T> p2,
+                                                                                                  int ntiles1, int K,
+                                                                                                  int kparts) {
   using Tile = GemmTile<T, 64, 64, 2, 2>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  const bool second = (int)blockIdx.x >= ntiles1;
+  const SplitProb<T> p = second ? p2 : p1;
+  const int tile = second ? (int)blockIdx.x - ntiles1 : (int)blockIdx.x;
+  const int M = p.M, N = p.N;
   const int ntn = (N + 63) / 64;
-  const int n0 = (blockIdx.x % ntn) * 64;
-  const int m0 = (blockIdx.x / ntn) * 64;
+  const int n0 = (tile % ntn) * 64;
+  const int m0 = (tile / ntn) * 64;
   const int kp = blockIdx.y;
   const int kslices = K / Tile::kBK;
   const int s0 = kp * kslices / kparts, s1 = (kp + 1) * kslices / kparts;
   const int koff = s0 * Tile::kBK;
   Tile t;
-  t.set_a([&](int r) -> const T* { return A + (size_t)min(m0 + r, M - 1) * lda + koff; });
-  t.set_b([&](int r) -> const T* { return B + (size_t)min(n0 + r, N - 1) * ldb + koff; });
+  t.set_a([&](int r) -> const T* { return p.A + (size_t)min(m0 + r, M - 1) * p.lda + koff; });
+  t.set_b([&](int r) -> const T* { return p.B + (size_t)min(n0 + r, N - 1) * p.ldb + koff; });
   t.run(smem, s1 - s0);
-  float* pp = part + (size_t)kp * M * N;
+  float* pp = p.part + (size_t)kp * M * N;
   t.epilogue([&](int m, int n, const float* v) {
     if (m0 + m < M && n0 + n < N) store4(pp + (size_t)(m0 + m) * N + n0 + n, v);
   });
@@ -136,6 +152,37 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
   epi(i / N, i % N, v);
 }
 
+// The same reduction over two problems in one launch.
+template <class Epi1, class Epi2>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce2_kernel(const float* __restrict__ part1, int M1, int N1,
+                                                                  const float* __restrict__ part2, int M2, int N2,
+                                                                  int kparts, Epi1 epi1, Epi2 epi2) {
+  int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const bool second = i >= M1 * N1;
+  if (second) i -= M1 * N1;
+  const int M = second ? M2 : M1, N = second ? N2 : N1;
+  const float* part = second ? part2 : part1;
+  if (i >= M * N) return;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int kp = 0; kp < kparts; ++kp) {
+    float w[4];
+    load4(part + (size_t)kp * M * N + i, w);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] += w[c];
+  }
+  if (second) epi2(i / N, i % N, v);
+  else epi1(i / N, i % N, v);
+}
+
+// K parts for a split over `ntiles` 64 x 64 tiles holding `elems` outputs, or 1 when the
+// GEMM should not be split.
+static int splitk_parts(int ntiles, int K, int kBK, size_t elems, size_t part_bytes) {
+  int kparts = 1;
+  while (ntiles * kparts * 2 <= 512 && (K / kBK) / (kparts * 2) >= 4 && elems * kparts * 2 * sizeof(float) <= part_bytes)
+    kparts *= 2;
+  return kparts;
+}
+
 // Tile choice. GEMMs with few rows (decode) split K into parts reduced by a second
 // pass (they stream weights). Otherwise the tile is picked by a cost model: a CU runs two 128-row tiles at once,
 // so the cost of a tile shape is (rounds of 512 tiles) x (tile area); 128x96 wins when
@@ -149,13 +196,10 @@ static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, in
   const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
   if (M <= 64 && part) {
     const int ntiles = (int)t64;
-    int kparts = 1;
-    while (ntiles * kparts * 2 <= 512 && (K / kBK) / (kparts * 2) >= 4 &&
-           (size_t)M * N * kparts * 2 * sizeof(float) <= part_bytes)
-      kparts *= 2;
+    const int kparts = splitk_parts(ntiles, K, kBK, (size_t)M * N, part_bytes);
     if (kparts > 1) {
-      hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(ntiles, kparts), dim3(256), 0, s, A, lda, B, ldb, M, N, K, kparts,
-                         part);
+      const SplitProb<T> p{A, lda, B, ldb, M, N, part};
+      hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(ntiles, kparts), dim3(256), 0, s, p, p, ntiles, K, kparts);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(gemm_splitk_reduce_kernel<Epi>, dim3((M * N / 4 + 255) / 256), dim3(256), 0, s, part, M, N,
@@ -181,6 +225,42 @@ hipError_t launch_gemm_store(const T* A, int lda, const T* B, int ldb, int M, in
 }
 
 template <typename T>
+hipError_t launch_gemm_store_pair(const T* A1, int lda1, const T* B1, int ldb1, int M1, int N1, T* C1, int ldc1,
+                                  const T* A2, int lda2, const T* B2, int ldb2, int M2, int N2, T* C2, int ldc2, int K,
+                                  float* part, size_t part_bytes, hipStream_t s) {
+  constexpr int kBK = 128 / (int)sizeof(T);
+  const int t1 = ((M1 + 63) / 64) * ((N1 + 63) / 64), t2 = ((M2 + 63) / 64) * ((N2 + 63) / 64);
+  const size_t e1 = (size_t)M1 * N1, e2 = (size_t)M2 * N2;
+  const int kparts = (M1 <= 64 && M2 <= 64 && part) ? splitk_parts(t1 + t2, K, kBK, e1 + e2, part_bytes) : 1;
+  if (kparts == 1) {  // not worth a split: two ordinary launches
+    hipError_t e = launch_gemm_store<T>(A1, lda1, B1, ldb1, M1, N1, K, C1, ldc1, part, part_bytes, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_store<T>(A2, lda2, B2, ldb2, M2, N2, K, C2, ldc2, part, part_bytes, s);
+  }
+  const SplitProb<T> p1{A1, lda1, B1, ldb1, M1, N1, part}, p2{A2, lda2, B2, ldb2, M2, N2, part + e1 * kparts};
+  hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(t1 + t2, kparts), dim3(256), 0, s, p1, p2, t1, K, kparts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_splitk_reduce2_kernel<EpiStore<T>, EpiStore<T>>),
+                     dim3((unsigned)((e1 + e2) / 4 + 255) / 256), dim3(256), 0, s, p1.part, M1, N1, p2.part, M2, N2,
+                     kparts, EpiStore<T>{C1, ldc1}, EpiStore<T>{C2, ldc2});
+  return hipGetLastError();
+}
+
+template <typename T>
+int launch_gemm_parts(const T* A, int lda, const T* B, int ldb, int M, int N, int K, float* part, size_t part_bytes,
+                      hipStream_t s) {
+  constexpr int kBK = 128 / (int)sizeof(T);
+  if (M > 64 || !part) return 0;
+  const int ntiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int kparts = splitk_parts(ntiles, K, kBK, (size_t)M * N, part_bytes);
+  if (kparts == 1) return 0;
+  const SplitProb<T> p{A, lda, B, ldb, M, N, part};
+  hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(ntiles, kparts), dim3(256), 0, s, p, p, ntiles, K, kparts);
+  return hipGetLastError() == hipSuccess ? kparts : -1;
+}
+
+template <typename T>
 hipError_t launch_gemm_merge(const T* O, const T* Wo, int M, int H, int K, const float* x, const T* hsb, const T* hss,
                              const T* rb, const T* rs, float* h, T* a_tap, float* part, size_t part_bytes,
                              hipStream_t s) {
@@ -199,7 +279,10 @@ hipError_t launch_gemm_router_in(const T* hn, const T* Wd, int M, int R, int H, 
   template hipError_t launch_gemm_merge<T>(const T*, const T*, int, int, int, const float*, const T*, const T*,      \
                                            const T*, const T*, float*, T*, float*, size_t, hipStream_t);             \
   template hipError_t launch_gemm_router_in<T>(const T*, const T*, int, int, int, const T*, const T*, const T*, T*, \
-                                               float*, size_t, hipStream_t);
+                                               float*, size_t, hipStream_t);                                         \
+  template hipError_t launch_gemm_store_pair<T>(const T*, int, const T*, int, int, int, T*, int, const T*, int,      \
+                                                const T*, int, int, int, T*, int, int, float*, size_t, hipStream_t); \
+  template int launch_gemm_parts<T>(const T*, int, const T*, int, int, int, int, float*, size_t, hipStream_t);
 ZAYA_INST(bf16_t)
 ZAYA_INST(float)
 #undef ZAYA_INST

@@ -21,6 +21,24 @@ hipError_t launch_embed(const int32_t* ids, const T* table, const T* shift, cons
 template <typename T>
 hipError_t launch_gemm_store(const T* A, int lda, const T* B, int ldb, int M, int N, int K, T* C, int ldc,
                              float* part, size_t part_bytes, hipStream_t s);
+// Decode helpers (at most 64 rows). Two store GEMMs with the same K in one split-K pass
+// and one reduction pass (two plain launches when a split does not pay).
+template <typename T>
+hipError_t launch_gemm_store_pair(const T* A1, int lda1, const T* B1, int ldb1, int M1, int N1, T* C1, int ldc1,
+                                  const T* A2, int lda2, const T* B2, int ldb2, int M2, int N2, T* C2, int ldc2, int K,
+                                  float* part, size_t part_bytes, hipStream_t s);
+// Only the split-K partial products [kparts][M][N] into part; returns kparts (> 1), 0 when
+// the GEMM is not split (nothing launched), -1 on a launch error.
+template <typename T>
+int launch_gemm_parts(const T* A, int lda, const T* B, int ldb, int M, int N, int K, float* part, size_t part_bytes,
+                      hipStream_t s);
+// Sum of the o_proj partials, the attention merge (as the merge epilogue) and the
+// post-attention RMSNorm of the result, one wave per row: writes h (and the
+// attention_output tap) and hn.
+template <typename T>
+hipError_t launch_merge_norm_parts(const float* part, int kparts, int rows, int H, const float* x, const T* hsb,
+                                   const T* hss, const T* rb, const T* rs, float* h, T* a_tap, const T* g2, T* hn,
+                                   float eps, hipStream_t s);
 template <typename T>
 hipError_t launch_gemm_merge(const T* O, const T* Wo, int M, int H, int K, const float* x, const T* hsb, const T* hss,
                              const T* rb, const T* rs, float* h, T* a_tap, float* part, size_t part_bytes,

@@ -93,6 +93,96 @@ hipError_t launch_rmsnorm_stream(const float* x, const T* g, T* out, int rows, i
   return hipGetLastError();
 }
 
+// Decode tail of the attention half, one workgroup per row (few rows, so the row is
+// spread over 256 threads): o = rnd(sum of the split-K partials, in part order), the
+// attention merge exactly as the o_proj merge epilogue (attention_output =
+// rnd(rnd(o + hsb) * hss); h = f32(f32(x + rb) * rs) + attention_output), then the
+// post-attention RMSNorm of h as rmsnorm_stream_kernel computes it (the sum of squares
+// reduced over the workgroup). Thread t owns columns 4t + 1024 i .. +3.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_norm_parts_kernel(const float* __restrict__ part, int kparts, int rows,
+                                                               int H, const float* __restrict__ x,
+                                                               const T* __restrict__ hsb, const T* __restrict__ hss,
+                                                               const T* __restrict__ rb, const T* __restrict__ rs,
+                                                               float* __restrict__ h, T* __restrict__ a_tap,
+                                                               const T* __restrict__ g2, T* __restrict__ hn,
+                                                               float eps) {
+  constexpr int NG = 4;  // H <= 4096
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float o[NG][4], xs[NG][4], b1[NG][4], s1[NG][4], b2[NG][4], s2[NG][4];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int n = min((int)threadIdx.x * 4 + i * 1024, H - 4);  // clamped: columns past H are never stored
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[i][c] = 0.f;
+    load4(x + (size_t)row * H + n, xs[i]);
+    load4(hsb + n, b1[i]);
+    load4(hss + n, s1[i]);
+    load4(rb + n, b2[i]);
+    load4(rs + n, s2[i]);
+  }
+#pragma unroll 2
+  for (int kp = 0; kp < kparts; ++kp) {
+    float w[NG][4];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) load4(part + ((size_t)kp * rows + row) * H + min((int)threadIdx.x * 4 + i * 1024, H - 4), w[i]);
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[i][c] += w[i][c];
+  }
+  float v[NG][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int n = (int)threadIdx.x * 4 + i * 1024;
+    float at[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float oc = Act<T>::rnd(o[i][c]);
+      at[c] = Act<T>::rnd(Act<T>::rnd(oc + b1[i][c]) * s1[i][c]);
+      v[i][c] = fadd(fmul(fadd(xs[i][c], b2[i][c]), s2[i][c]), at[c]);
+    }
+    if (n < H) {
+      store4(h + (size_t)row * H + n, v[i]);
+      if (a_tap) store4(a_tap + (size_t)row * H + n, at);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[i][c] = Act<T>::rnd(v[i][c]);
+        ss += v[i][c] * v[i][c];
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int n = (int)threadIdx.x * 4 + i * 1024;
+    if (n >= H) continue;
+    float gv[4], out[4];
+    load4(g2 + n, gv);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = Act<T>::rnd(gv[c] * Act<T>::rnd(v[i][c] * inv));
+    store4(hn + (size_t)row * H + n, out);
+  }
+}
+
+template <typename T>
+hipError_t launch_merge_norm_parts(const float* part, int kparts, int rows, int H, const float* x, const T* hsb,
+                                   const T* hss, const T* rb, const T* rs, float* h, T* a_tap, const T* g2, T* hn,
+                                   float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (H > 4096 || H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((merge_norm_parts_kernel<T>), dim3(rows), dim3(256), 0, s, part, kparts, rows, H, x, hsb, hss, rb,
+                     rs, h, a_tap, g2, hn, eps);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* table, const T* shift, const T* scale, float* x0, T* tap,
                         int rows, int H, int vocab, hipStream_t s) {
@@ -113,6 +203,12 @@ hipError_t launch_fill_i32(int32_t* p, int n, int v, hipStream_t s) {
   return hipGetLastError();
 }
 
+template hipError_t launch_merge_norm_parts<bf16_t>(const float*, int, int, int, const float*, const bf16_t*,
+                                                    const bf16_t*, const bf16_t*, const bf16_t*, float*, bf16_t*,
+                                                    const bf16_t*, bf16_t*, float, hipStream_t);
+template hipError_t launch_merge_norm_parts<float>(const float*, int, int, int, const float*, const float*, const float*,
+                                                   const float*, const float*, float*, float*, const float*, float*,
+                                                   float, hipStream_t);
 template hipError_t launch_rmsnorm_stream<bf16_t>(const float*, const bf16_t*, bf16_t*, int, int, float, hipStream_t);
 template hipError_t launch_rmsnorm_stream<float>(const float*, const float*, float*, int, int, float, hipStream_t);
 template hipError_t launch_embed<bf16_t>(const int32_t*, const bf16_t*, const bf16_t*, const bf16_t*, float*, bf16_t*,

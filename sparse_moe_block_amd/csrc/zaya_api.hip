@@ -223,10 +223,15 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   // a2: q/k/v projections (+ the delayed value of the token before this call)
   HIPCHK(mark(1));
   float* gpart = p.gpart_bytes ? (float*)(ws + p.gpart) : nullptr;
-  HIPCHK(launch_gemm_store<T>(xn, H, W(w->W_qkv), H, T_, QR, H, P, QR, gpart, p.gpart_bytes, st));
   const T* Wvd = W(w->W_qkv) + (size_t)(nh * d + nkv * d + nkv * d / 2) * H;
-  if (any_cached)
-    HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, gpart, p.gpart_bytes, st));
+  if (any_cached && T_ <= 64) {  // few rows: both products share one split-K pass
+    HIPCHK(launch_gemm_store_pair<T>(xn, H, W(w->W_qkv), H, T_, QR, P, QR, prev_hs, H, Wvd, H, B, nkv * d / 2, vdp,
+                                     nkv * d / 2, H, gpart, p.gpart_bytes, st));
+  } else {
+    HIPCHK(launch_gemm_store<T>(xn, H, W(w->W_qkv), H, T_, QR, H, P, QR, gpart, p.gpart_bytes, st));
+    if (any_cached)
+      HIPCHK(launch_gemm_store<T>(prev_hs, H, Wvd, H, B, nkv * d / 2, H, vdp, nkv * d / 2, gpart, p.gpart_bytes, st));
+  }
   // a3: convolution, residual, QK norm, temperature, rotary, value halves, state
   HIPCHK(mark(2));
   T* y2 = nullptr;
@@ -254,12 +259,22 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(tap_copy(tp.attention_premix, O, (size_t)T_ * nh * d * A));
   // a5: o_proj + attention merge
   HIPCHK(mark(4));
-  HIPCHK(launch_gemm_merge<T>(O, W(w->W_o), T_, H, nh * d, x, W(w->a_hsb), W(w->a_hss), W(w->a_rb), W(w->a_rs), h,
-                              (T*)tp.attention_output, gpart, p.gpart_bytes, st));
-  HIPCHK(tap_copy(tp.layer_mid, h, (size_t)T_ * H * 4));
-  // a6: post-attention RMSNorm
-  HIPCHK(mark(5));
-  HIPCHK(launch_rmsnorm_stream<T>(h, W(w->ln2_g), hn, T_, H, c->rms_eps, st));
+  // few rows: split-K partials, then one pass that sums them, merges and norms (a5 + a6)
+  const int oparts = launch_gemm_parts<T>(O, nh * d, W(w->W_o), nh * d, T_, H, nh * d, gpart, p.gpart_bytes, st);
+  if (oparts < 0) return fail(ZAYA_EHIP, "o_proj split-K launch failed");
+  if (oparts > 1) {
+    HIPCHK(launch_merge_norm_parts<T>(gpart, oparts, T_, H, x, W(w->a_hsb), W(w->a_hss), W(w->a_rb), W(w->a_rs), h,
+                                      (T*)tp.attention_output, W(w->ln2_g), hn, c->rms_eps, st));
+    HIPCHK(tap_copy(tp.layer_mid, h, (size_t)T_ * H * 4));
+    HIPCHK(mark(5));
+  } else {
+    HIPCHK(launch_gemm_merge<T>(O, W(w->W_o), T_, H, nh * d, x, W(w->a_hsb), W(w->a_hss), W(w->a_rb), W(w->a_rs), h,
+                                (T*)tp.attention_output, gpart, p.gpart_bytes, st));
+    HIPCHK(tap_copy(tp.layer_mid, h, (size_t)T_ * H * 4));
+    // a6: post-attention RMSNorm
+    HIPCHK(mark(5));
+    HIPCHK(launch_rmsnorm_stream<T>(h, W(w->ln2_g), hn, T_, H, c->rms_eps, st));
+  }
   HIPCHK(tap_copy(tp.mlp_norm_output, hn, (size_t)T_ * H * A));
   // a7: router down_proj + carried state
   HIPCHK(mark(6));
