@@ -497,8 +497,13 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
       const int key = ch / CPR, col = (ch % CPR) * E16;
       const bool ok = ch < NCH && t0 + key < c_hi;
       const size_t slot = a.ring ? (size_t)((t0 + key) % a.cap) : (size_t)(t0 + key);  // ring: p % cap
-      kr[i] = ok ? *reinterpret_cast<const uint4*>(Kb + slot * D + col) : make_uint4(0, 0, 0, 0);
-      vr[i] = ok ? *reinterpret_cast<const uint4*>(Vb + slot * D + col) : make_uint4(0, 0, 0, 0);
+      // the cache is streamed once per step: non-temporal loads keep it out of the caches
+      const u32x4 kq = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kb + slot * D + col))
+                          : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vq = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + slot * D + col))
+                          : u32x4{0u, 0u, 0u, 0u};
+      kr[i] = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+      vr[i] = make_uint4(vq[0], vq[1], vq[2], vq[3]);
     }
   };
   const int t_first = (c_lo / 64) * 64;

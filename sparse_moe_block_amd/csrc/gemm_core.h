@@ -20,7 +20,9 @@
 
 namespace zaya {
 
-template <typename T, int BM, int BN, int WM, int WN>
+// STREAM_B: the B rows are read once per launch (weights of a few-token expert item):
+// their loads are non-temporal so they do not evict data that is reused.
+template <typename T, int BM, int BN, int WM, int WN, bool STREAM_B = false>
 struct GemmTile {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
@@ -91,7 +93,10 @@ struct GemmTile {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + off);
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + off);
+    for (int i = 0; i < kBChunks; ++i) {
+      if constexpr (STREAM_B) rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pb[i] + off));
+      else rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + off);
+    }
   }
 
   __device__ __forceinline__ static void store_slice(char* buf, const u32x4* ra, const u32x4* rb) {

@@ -179,6 +179,10 @@ hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, 
 
 // ----------------------------------------------------------------------------- grouped GEMMs
 
+// Expert items of 16 rows read each weight tile once: their weight loads may bypass the
+// caches (non-temporal).
+constexpr bool kStreamFewRows = true;
+
 // Work items of a grouped GEMM are (expert, column tile, row tile), expert by expert,
 // then column tile, row tile fastest. They are dealt to the 8 XCDs in contiguous runs
 // (workgroup b runs on XCD b % 8), so at any time the workgroups of one XCD work on
@@ -222,7 +226,7 @@ template <typename T, int BM, int WM, int WN, int BN = 128>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
   constexpr int CN = BN / 2;  // activation columns per item
-  using Tile = GemmTile<T, BM, BN, WM, WN>;
+  using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
   static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
   int e, r0, n_e, j;  // j: activation columns [CN j, CN j + CN)
@@ -265,7 +269,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
 template <typename T, int BM, int WM, int WN, int BN = 128>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
-  using Tile = GemmTile<T, BM, BN, WM, WN>;
+  using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
   int e, r0, n_e, c;
   if (!moe_item(a.offsets, a.E, BM, a.H / BN, e, r0, n_e, c)) return;
@@ -347,6 +351,7 @@ hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
 // operands), which only permutes the terms of each dot product.
 constexpr int kF8Tok = 16;
 constexpr int kF8Ahead = 8;
+constexpr bool kF8Stream = false;  // non-temporal weight loads measured slower for FP8 items (decode gate/up 40 vs 31 us)
 
 __device__ __forceinline__ void f8x16_to_bf16(const u32x4 q, bf16x8_t& lo, bf16x8_t& hi) {
   u32x4 a, b;
@@ -365,7 +370,9 @@ __device__ __forceinline__ void f8x16_to_bf16(const u32x4 q, bf16x8_t& lo, bf16x
   hi = __builtin_bit_cast(bf16x8_t, b);
 }
 
-template <bool GATEUP>
+// STREAM: every weight tile is read by one item (few tokens per expert): non-temporal
+// weight loads.
+template <bool GATEUP, bool STREAM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void moe_f8_kernel(MoeArgs<bf16_t> a) {
   extern __shared__ __attribute__((aligned(16))) char xs[];  // kF8Tok rows x (K bf16 + 16 bytes)
   const int K = GATEUP ? a.H : a.I;
@@ -385,12 +392,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   const uint8_t* w0 = W + (size_t)n_row * K + grp * 16;
   const uint8_t* w1 = W + (size_t)(GATEUP ? a.I + n_row : n_row) * K + grp * 16;
   const int nds = K / 64;
+  auto wload = [](const uint8_t* p) -> u32x4 {
+    if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+  };
   u32x4 q0[kF8Ahead], q1[kF8Ahead];
 #pragma unroll
   for (int p = 0; p < kF8Ahead; ++p) {
     const int s = min(p, nds - 1);
-    q0[p] = *reinterpret_cast<const u32x4*>(w0 + (size_t)s * 64);
-    if (GATEUP) q1[p] = *reinterpret_cast<const u32x4*>(w1 + (size_t)s * 64);
+    q0[p] = wload(w0 + (size_t)s * 64);
+    if (GATEUP) q1[p] = wload(w1 + (size_t)s * 64);
   }
 
   // stage the token rows (rows past the tile repeat its last row; never stored)
@@ -437,8 +448,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         }
         // refill this slot kF8Ahead steps ahead (past the end: the last step again)
         const int sn = min(s + kF8Ahead, nds - 1);
-        q0[p] = *reinterpret_cast<const u32x4*>(w0 + (size_t)sn * 64);
-        if (GATEUP) q1[p] = *reinterpret_cast<const u32x4*>(w1 + (size_t)sn * 64);
+        q0[p] = wload(w0 + (size_t)sn * 64);
+        if (GATEUP) q1[p] = wload(w1 + (size_t)sn * 64);
       }
     }
   }
@@ -486,11 +497,17 @@ static hipError_t launch_f8(const MoeArgs<bf16_t>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
   const int K = GATEUP ? a.H : a.I;
   const size_t lds = (size_t)kF8Tok * (K * 2 + 16);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_f8_kernel<GATEUP>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_f8_kernel<GATEUP, false>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static const hipError_t attr_s = hipFuncSetAttribute((const void*)moe_f8_kernel<GATEUP, true>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(moe_f8_kernel<GATEUP>, dim3(moe_grid(a.ntok, a.E, kF8Tok, (GATEUP ? a.I : a.H) / 64)),
-                     dim3(256), lds, s, a);
+  if (attr_s != hipSuccess) return attr_s;
+  const dim3 grid(moe_grid(a.ntok, a.E, kF8Tok, (GATEUP ? a.I : a.H) / 64));
+  if (a.ntok <= kF8Tok * a.E && kF8Stream)  // about one token tile per expert: weights streamed once
+    hipLaunchKernelGGL((moe_f8_kernel<GATEUP, true>), grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((moe_f8_kernel<GATEUP, false>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
