@@ -45,7 +45,10 @@ struct AttnLds {
   static constexpr int kVBytes = D * kVRow;
   static constexpr int kBytes = kKBytes + kVBytes;
   __device__ __forceinline__ static int koff(int key, int chunk) {
-    return key * kKRow + ((chunk ^ (key & (kKChunksRow - 1))) << 4);
+    // 16 chunks per row (bf16, d = 128): the key's low bits, plus (key / 16) % 4 in the
+    // upper bits, measured faster for the fragment reads (127 vs 115 TB/s)
+    const int m = kKChunksRow == 16 ? (key & 15) ^ (((key >> 4) & 3) << 2) : (key & (kKChunksRow - 1));
+    return key * kKRow + ((chunk ^ m) << 4);
   }
   // Measured on gfx950 (fragment reads: 16 dim rows x 4 unit columns per lane group;
   // transposing writes: 8 rows of one unit per lane): this mask reads at ~97 TB/s over
