@@ -22,6 +22,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # register arrays stay in registers: the compiler would otherwise move some of them
+    # to spare LDS, adding LDS round trips to the attention loops
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -19,6 +19,8 @@
 // tiles staged through LDS with 16-byte coalesced loads, scores with one lane per key,
 // the weighted sum with one lane per pair of dims — then a combine pass merges the
 // chunks' (max, sum, partial output) triples.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -178,10 +180,11 @@ struct QTile {
   int q0, nq, qp_min, qp_max, kt_begin, n, nc;
 };
 
+template <int QW = 32>
 __device__ __forceinline__ QTile qtile(int qblk, int S, int L0, int W, int NC) {
   QTile r;
-  r.q0 = qblk * 32;
-  r.nq = min(32, S - r.q0);
+  r.q0 = qblk * QW;
+  r.nq = min(QW, S - r.q0);
   r.qp_min = L0 + r.q0;
   r.qp_max = L0 + r.q0 + r.nq - 1;
   const int klo = W >= 0 ? max(0, r.qp_min - W) : 0;
@@ -390,22 +393,22 @@ struct CombineShape {
   static constexpr int kThreads = kRowsPerWg * G * kNJ;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int QW = 32>
 __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a, const float* __restrict__ part,
                                                                    int NC) {
   using CS = CombineShape<D, G>;
-  const int nqb = (a.S + 31) / 32;
-  const int qblk = blockIdx.x / (32 / CS::kRowsPerWg), g = blockIdx.y, b = blockIdx.z;
+  const int nqb = (a.S + QW - 1) / QW;
+  const int qblk = blockIdx.x / (QW / CS::kRowsPerWg), g = blockIdx.y, b = blockIdx.z;
   const int L0 = cached_len(a.cache_len, b);
-  const QTile qt = qtile(qblk, a.S, L0, a.window, NC);
+  const QTile qt = qtile<QW>(qblk, a.S, L0, a.window, NC);
   if (qt.nc == 1) return;
   const int j = threadIdx.x % CS::kNJ, wave = (threadIdx.x / CS::kNJ) % G;
-  const int row = (blockIdx.x % (32 / CS::kRowsPerWg)) * CS::kRowsPerWg + threadIdx.x / (CS::kNJ * G);
+  const int row = (blockIdx.x % (QW / CS::kRowsPerWg)) * CS::kRowsPerWg + threadIdx.x / (CS::kNJ * G);
   if (row >= qt.nq) return;
   const int h = g * G + wave;
   const size_t unit0 = (((size_t)b * a.nkv + g) * nqb + qblk) * NC;
-  const size_t ustride = (size_t)G * 32 * (D + 2);
-  const float* base = part + (unit0 * G + wave) * 32 * (D + 2) + (size_t)row * (D + 2);
+  const size_t ustride = (size_t)G * QW * (D + 2);
+  const float* base = part + (unit0 * G + wave) * QW * (D + 2) + (size_t)row * (D + 2);
   // chunks in groups of four, loads issued together (past the last chunk they re-read it)
   float M = -INFINITY;
   for (int c0 = 0; c0 < qt.nc; c0 += 4) {
@@ -437,6 +440,296 @@ __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a
   T* orow = a.O + (((size_t)b * a.S + qt.q0 + row) * a.nh + h) * D + 4 * j;
   float o4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
   store4(orow, o4);
+}
+
+// ----------------------------------------------------------------------------- prefill, bf16, d = 128
+//
+// A second prefill kernel for bf16 with head_dim 128: one workgroup per CU of 2 G waves,
+// two per query head of the KV group, each wave 32 of the workgroup's 64 queries (two
+// waves per SIMD). Both products use the 32x32x16 MFMA:
+//   S^T = K Q^T  in 32-key x 32-query blocks: lane l holds query l % 32 and the keys
+//                8 (r / 4) + 4 (l / 32) + r % 4, r < 16, of the block;
+//   O^T = V^T P^T in 32-dim x 32-query blocks over 16-key steps: the B operand of step
+//                ks is eight of the lane's score registers as they are (registers
+//                8 (ks % 2) .. +8 of key block ks / 2), and the V^T rows are read in the
+//                same key order (4-key units 4 ks + l / 32 and 4 ks + 2 + l / 32).
+// Each K/V tile in LDS serves 2 G waves. K tiles go from global memory straight into
+// LDS (global_load_lds, the swizzle applied on the global side); V goes through registers
+// and is transposed as it is written. Two LDS tile buffers, declared as two arrays so the
+// compiler's wait tracking sees that the direct loads into one cannot alias reads of the
+// other (one array made it wait for the next tile before every read of the current one:
+// 74.6 vs 72.0 us). The loop is unrolled by two, so every fragment read is a per-lane
+// offset (computed once) plus an immediate.
+namespace pf64 {
+constexpr int kQW = 64;                  // queries per workgroup (per head)
+constexpr int kD = 128;
+constexpr int kKRow = kD * 2;            // bytes per K row (bf16)
+constexpr int kVRow = 64 * 2;            // bytes per V^T row (64 keys)
+constexpr int kKBytes = 64 * kKRow;
+constexpr int kBuf = kKBytes + kD * kVRow;
+// Measured on gfx950 for these fragment reads (32 key rows of one 16-byte chunk per
+// half wave): chunk c of key k stored at c ^ (k % 16) reads conflict-free (118 TB/s);
+// the swizzle of the 16x16 kernel drops to 69 TB/s here.
+__device__ __forceinline__ int koff(int key, int chunk) { return key * kKRow + ((chunk ^ (key & 15)) << 4); }
+// V^T: 8-byte unit u (4 keys) of dim row d at u ^ ((d / 2) % 16): reads 96 TB/s, the
+// transposing writes 38 TB/s (measured); depending on d % 32 only, it leaves the
+// fragment address of dim block db at a fixed offset db * 32 rows from block 0's.
+__device__ __forceinline__ int voff(int d, int unit) { return d * kVRow + ((unit ^ ((d >> 1) & 15)) << 3); }
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+__device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+}  // namespace pf64
+
+template <int G>
+__global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill64_kernel(
+    AttnArgs<bf16_t> a, float* __restrict__ part, int NC) {
+  using namespace pf64;
+  constexpr int NT = 128 * G;
+  constexpr int VD = NT >= 512 ? 4 : 8;     // dims per V task (4 keys x VD dims)
+  constexpr int VT = 64 * kD / (4 * VD) / NT;  // V tasks per thread
+  constexpr int VW = VD / 4;                // 8-byte words per key row of a task
+  __shared__ __attribute__((aligned(1024))) char lds0[kBuf];
+  __shared__ __attribute__((aligned(1024))) char lds1[kBuf];
+
+  const int nqb = (a.S + kQW - 1) / kQW;
+  const int c = blockIdx.x % NC;
+  const int qblk = nqb - 1 - (int)(blockIdx.x / NC);
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int S = a.S, L0 = cached_len(a.cache_len, b), W = a.window;
+  const QTile qt = qtile<kQW>(qblk, S, L0, W, NC);
+  if (c >= qt.nc) return;
+  const int kt0 = qt.kt_begin + c * qt.n / qt.nc;
+  const int kt1 = qt.kt_begin + (c + 1) * qt.n / qt.nc;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int hg = wave % G, qh = wave / G;  // head within the group, query half
+  const int h = g * G + hg;
+  const int row = qh * 32 + l32;           // this lane's query within the tile
+  const int q0 = qt.q0, qp_min = qt.qp_min, qp_max = qt.qp_max;
+  const int qp = L0 + q0 + row;
+  const int kvalid = L0 + S;
+  const bf16_t* Kb = a.K + ((size_t)b * a.nkv + g) * a.cap * kD;
+  const bf16_t* Vb = a.V + ((size_t)b * a.nkv + g) * a.cap * kD;
+  const float sscale = kLog2e / sqrtf((float)kD);
+
+  // this lane's query (zero past S): dims 16 ds + 8 hl .. + 8
+  uint4 qf[8];
+  {
+    const int t = q0 + row;
+    const bf16_t* qrow = a.Q + (((size_t)b * S + min(t, S - 1)) * a.nh + h) * kD + 8 * hl;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * ds);
+      qf[ds] = t < S ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // fragment offsets within a buffer: K for step ds (key block 0; block 1 is 32 rows on),
+  // V^T for step ks, low/high unit (dim block 0; block db is 32 db rows on)
+  int ko[8], vo[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds) ko[ds] = koff(l32, 2 * ds + hl);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    vo[2 * ks] = kKBytes + voff(l32, 4 * ks + hl);
+    vo[2 * ks + 1] = kKBytes + voff(l32, 4 * ks + 2 + hl);
+  }
+
+  // Tile loads. Key rows past kvalid - 1 re-read that row: those keys come after every
+  // query of the call, so their scores are masked and their probabilities are exactly 0.
+  auto issue_k = [&](char* buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < 8 / G; ++j) {
+      const int kr0 = (wave * (8 / G) + j) * 4;
+      const int key = kr0 + (lane >> 4);
+      const int chunk = (lane & 15) ^ (key & 15);
+      const bf16_t* src = Kb + (size_t)min(k0 + key, kvalid - 1) * kD + chunk * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + kr0 * kKRow), 16, 0, 0);
+    }
+  };
+  uint2 vr[VT][4][VW];  // task i, key kk: VD dims as 8-byte words
+  auto load_v = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < VT; ++i) {
+      const int task = (int)threadIdx.x + i * NT;
+      const int q4 = task / (kD / VD), dq = task % (kD / VD);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16_t* src = Vb + (size_t)min(k0 + 4 * q4 + kk, kvalid - 1) * kD + dq * VD;
+        if constexpr (VW == 2) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src);
+          vr[i][kk][0] = make_uint2(v.x, v.y);
+          vr[i][kk][1] = make_uint2(v.z, v.w);
+        } else {
+          vr[i][kk][0] = *reinterpret_cast<const uint2*>(src);
+        }
+      }
+    }
+  };
+  // V^T row d = VD dq + j, unit q4: keys 4 q4 .. +3 of dim d, packed two keys a word
+  auto store_v = [&](char* buf) {
+    char* vt = buf + kKBytes;
+#pragma unroll
+    for (int i = 0; i < VT; ++i) {
+      const int task = (int)threadIdx.x + i * NT;
+      const int q4 = task / (kD / VD), dq = task % (kD / VD);
+#pragma unroll
+      for (int j = 0; j < VD; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        auto word = [&](int kk) -> uint32_t {
+          const uint2 q = vr[i][kk][j >> 2];
+          return ((j >> 1) & 1) ? q.y : q.x;
+        };
+        uint2 w;
+        w.x = __builtin_amdgcn_perm(word(1), word(0), sel);
+        w.y = __builtin_amdgcn_perm(word(3), word(2), sel);
+        *reinterpret_cast<uint2*>(vt + voff(dq * VD + j, q4)) = w;
+      }
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // one key tile j in LDS buffer B; with `more`, tile j + 1 loads into the other buffer
+  auto step = [&](auto buf_tag, int j) {
+    constexpr int B = decltype(buf_tag)::value;
+    const char* buf = B == 0 ? lds0 : lds1;
+    char* other = B == 0 ? lds1 : lds0;
+    const bool more = j + 1 < kt1;
+    if (more) {
+      issue_k(other, (j + 1) * 64);
+      load_v((j + 1) * 64);
+    }
+    const int k0 = j * 64;
+    // S^T = K Q^T
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(buf + ko[ds] + kb * 32 * kKRow);
+        s[kb] = mma(kf, qf[ds], s[kb]);
+      }
+    // mask where the tile cuts the causal / window band; running max; rescale
+    const bool full = (k0 + 63 <= qp_min) && (W < 0 || qp_max - k0 <= W);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kp = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (kp > qp || (W >= 0 && qp - kp > W)) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float mc = m_new == -INFINITY ? 0.f : m_new * sscale;
+    if (__ballot(m_new != m_run)) {  // some row's maximum moved: rescale
+      const float alpha = __builtin_amdgcn_exp2f(m_run * sscale - mc);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    m_run = m_new;
+    // probabilities (exponent base 2, the 1/sqrt(d) log2(e) factor folded in), row sum,
+    // bf16 B fragments
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sscale, -mc));
+        s[kb][r] = pv;
+        ps += pv;
+      }
+    l_run += ps;
+    uint4 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb = ks >> 1, r0 = 8 * (ks & 1);
+      pf[ks] = make_uint4(pack_bf16x2(s[kb][r0], s[kb][r0 + 1]), pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]),
+                          pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]), pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]));
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(buf + vo[2 * ks] + db * 32 * kVRow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(buf + vo[2 * ks + 1] + db * 32 * kVRow);
+        o[db] = mma(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[ks], o[db]);
+      }
+    if (more) {
+      asm volatile("" ::: "memory");  // keep the stores (and their wait for the loads) here
+      store_v(other);
+    }
+    // this wave's direct K loads into the other buffer have landed before the barrier
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    __syncthreads();
+  };
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
+
+  issue_k(lds0, kt0 * 64);
+  load_v(kt0 * 64);
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  store_v(lds0);
+  __syncthreads();
+  for (int j = kt0; j < kt1; j += 2) {
+    step(Buf0{}, j);
+    if (j + 1 < kt1) step(Buf1{}, j + 1);
+  }
+
+  // lane holds O^T[d = 32 db + 8 (r / 4) + 4 hl + r % 4][its query]; the row sum is
+  // split over lanes l32 and l32 + 32
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const int t = q0 + row;
+  if (qt.nc == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (t < S) {
+      bf16_t* orow = a.O + (((size_t)b * S + t) * a.nh + h) * kD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float v[4] = {o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
+                        o[db][4 * gq + 3] * inv};
+          store4(orow + db * 32 + 8 * gq + 4 * hl, v);
+        }
+    }
+  } else {
+    float* pr = part + (((((size_t)b * a.nkv + g) * nqb + qblk) * NC + c) * G + hg) * kQW * (kD + 2) +
+                (size_t)row * (kD + 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float v[4] = {o[db][4 * gq], o[db][4 * gq + 1], o[db][4 * gq + 2], o[db][4 * gq + 3]};
+        store4(pr + db * 32 + 8 * gq + 4 * hl, v);
+      }
+    if (hl == 0) {  // the combine pass works in the exponent's units: m * scale
+      pr[kD] = m_run == -INFINITY ? -INFINITY : m_run * sscale;
+      pr[kD + 1] = l;
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------- decode
@@ -657,6 +950,16 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnArgs<T> a, 
 
 template <typename T, int D, int G>
 static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && D == 128 && G <= 4) {
+    const int nqb = (a.S + pf64::kQW - 1) / pf64::kQW;
+    hipLaunchKernelGGL((attn_prefill64_kernel<G>), dim3(nqb * NC, a.nkv, a.B), dim3(128 * G), 0, s, a, part, NC);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || NC == 1) return e;
+    using CS = CombineShape<D, G>;
+    hipLaunchKernelGGL((attn_prefill_combine_kernel<T, D, G, pf64::kQW>),
+                       dim3(nqb * (pf64::kQW / CS::kRowsPerWg), a.nkv, a.B), dim3(CS::kThreads), 0, s, a, part, NC);
+    return hipGetLastError();
+  }
   const int nqb = (a.S + 31) / 32;
   hipLaunchKernelGGL((attn_prefill_kernel<T, D, G>), dim3(nqb * NC, a.nkv, a.B), dim3(64 * G), 0, s, a, part, NC);
   hipError_t e = hipGetLastError();
@@ -712,10 +1015,11 @@ int attn_prefill_chunks(int S, int max_cache_len, int window) {
   return nc < 1 ? 1 : (nc > 16 ? 16 : nc);
 }
 
+// Sized for 64-query tiles, which covers the 32-query tiles of the other kernel too.
 size_t attn_prefill_part_bytes(int B, int S, int nkv, int G, int d, int NC) {
   if (NC <= 1) return 0;
-  const size_t nqb = (size_t)(S + 31) / 32;
-  return (size_t)B * nkv * nqb * NC * G * 32 * (d + 2) * sizeof(float);
+  const size_t rows = (size_t)(S + 63) / 64 * 64;
+  return (size_t)B * nkv * rows * NC * G * (d + 2) * sizeof(float);
 }
 
 template <typename T>
