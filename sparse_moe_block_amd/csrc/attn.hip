@@ -27,7 +27,11 @@
 namespace zaya {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPrefillChunkTiles = 16;  // longest run of 64-key tiles one prefill unit handles
+// Longest run of 64-key tiles one prefill unit handles: 16 for the 32-query kernel, 22
+// for the 64-query one (at 4096 tokens: three chunks for the longest query tile, 68.7 us
+// for kernel and merge against 72.0 us with four and 81.0 with five).
+constexpr int kPrefillChunkTiles = 16;
+constexpr int kPrefill64ChunkTiles = 22;
 
 // ----------------------------------------------------------------------------- prefill
 
@@ -1005,13 +1009,17 @@ hipError_t launch_attn_prefill(const AttnArgs<T>& a, float* part, int NC, hipStr
   ZAYA_DISPATCH_DG(launch_prefill_dg, a, part, NC, s);
 }
 
-// Chunks per query tile: enough that no unit exceeds kPrefillChunkTiles key tiles of the
+int attn_prefill_chunk_tiles(int act_bytes, int d, int G) {
+  return act_bytes == 2 && d == 128 && G <= 4 ? kPrefill64ChunkTiles : kPrefillChunkTiles;
+}
+
+// Chunks per query tile: enough that no unit exceeds chunk_tiles key tiles of the
 // longest query tile (capped at 16).
-int attn_prefill_chunks(int S, int max_cache_len, int window) {
+int attn_prefill_chunks(int S, int max_cache_len, int window, int chunk_tiles) {
   const int qp_max = max_cache_len + S - 1;
   const int klo = window >= 0 ? (qp_max - 31 - window > 0 ? qp_max - 31 - window : 0) : 0;
   const int tiles = qp_max / 64 + 1 - klo / 64;
-  int nc = (tiles + kPrefillChunkTiles - 1) / kPrefillChunkTiles;
+  int nc = (tiles + chunk_tiles - 1) / chunk_tiles;
   return nc < 1 ? 1 : (nc > 16 ? 16 : nc);
 }
 

@@ -116,7 +116,10 @@ struct AttnArgs {
 };
 template <typename T>
 hipError_t launch_attn_prefill(const AttnArgs<T>& a, float* part, int NC, hipStream_t s);
-int attn_prefill_chunks(int S, int max_cache_len, int window);
+// key tiles per prefill unit of the kernel the shape selects, and the chunk count per
+// query tile that keeps units within it
+int attn_prefill_chunk_tiles(int act_bytes, int d, int G);
+int attn_prefill_chunks(int S, int max_cache_len, int window, int chunk_tiles);
 size_t attn_prefill_part_bytes(int B, int S, int nkv, int G, int d, int NC);
 template <typename T>
 // span: the largest number of positions from a sequence's 64-aligned window start (0

@@ -71,9 +71,11 @@ int check_config(const zaya_block_config* c) {
 }
 
 // Key-range chunks per query tile the prefill workspace has room for: what a call
-// without cached tokens needs, and at least 4 so calls after a cache can split too.
+// without cached tokens needs with the shorter of the kernels' chunk lengths, and at
+// least 4 so calls after a cache can split too.
+constexpr int kPrefillChunkTilesMin = 16;
 int prefill_chunks_ws(const zaya_block_config* c, int S) {
-  const int nc = attn_prefill_chunks(S, 0, c->sliding_window);
+  const int nc = attn_prefill_chunks(S, 0, c->sliding_window, kPrefillChunkTilesMin);
   return nc < 4 ? 4 : nc;
 }
 
@@ -253,7 +255,8 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
     HIPCHK(launch_attn_decode<T>(aa, (float*)(ws + p.part), max_len, st));
   else
     HIPCHK(launch_attn_prefill<T>(aa, (float*)(ws + p.part),
-                                  std::min(attn_prefill_chunks(S, max_len - S, c->sliding_window),
+                                  std::min(attn_prefill_chunks(S, max_len - S, c->sliding_window,
+                                                               attn_prefill_chunk_tiles((int)A, d, nh / nkv)),
                                            prefill_chunks_ws(c, S)),
                                   st));
   HIPCHK(tap_copy(tp.attention_premix, O, (size_t)T_ * nh * d * A));
