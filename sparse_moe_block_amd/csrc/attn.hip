@@ -475,10 +475,13 @@ constexpr int kBuf = kKBytes + kD * kVRow;
 // half wave): chunk c of key k stored at c ^ (k % 16) reads conflict-free (118 TB/s);
 // the swizzle of the 16x16 kernel drops to 69 TB/s here.
 __device__ __forceinline__ int koff(int key, int chunk) { return key * kKRow + ((chunk ^ (key & 15)) << 4); }
-// V^T: 8-byte unit u (4 keys) of dim row d at u ^ ((d / 2) % 16): reads 96 TB/s, the
-// transposing writes 38 TB/s (measured); depending on d % 32 only, it leaves the
-// fragment address of dim block db at a fixed offset db * 32 rows from block 0's.
-__device__ __forceinline__ int voff(int d, int unit) { return d * kVRow + ((unit ^ ((d >> 1) & 15)) << 3); }
+// V^T: 8-byte unit u (4 keys) of dim row d at u ^ vswz(d), the mask of the kernel above:
+// no bank conflicts for these 32-row fragment reads nor for the transposing writes of
+// 4-key x 8-dim tasks (measured with the LDS conflict counter; (d / 2) % 16 reads as
+// fast but its writes conflict). For d = 32 db + r (r < 32) it equals vswz(r) ^ 2 db,
+// so dim block db's fragment sits db * 32 rows after block 0's, at unit u ^ 2 db.
+__device__ __forceinline__ int vswz(int d) { return (((d >> 1) & 7) << 1) ^ ((d >> 4) & 7); }
+__device__ __forceinline__ int voff(int d, int unit) { return d * kVRow + ((unit ^ vswz(d)) << 3); }
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -491,9 +494,10 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     AttnArgs<bf16_t> a, float* __restrict__ part, int NC) {
   using namespace pf64;
   constexpr int NT = 128 * G;
-  constexpr int VD = NT >= 512 ? 4 : 8;     // dims per V task (4 keys x VD dims)
-  constexpr int VT = 64 * kD / (4 * VD) / NT;  // V tasks per thread
+  constexpr int VD = 8;                     // dims per V task (4 keys x 8 dims): 256 tasks
+  constexpr int VT = NT >= 256 ? 1 : 256 / NT;  // V tasks per thread (threads past 256 have none)
   constexpr int VW = VD / 4;                // 8-byte words per key row of a task
+  const bool v_task = NT <= 256 || threadIdx.x < 256;  // whole waves
   __shared__ __attribute__((aligned(1024))) char lds0[kBuf];
   __shared__ __attribute__((aligned(1024))) char lds1[kBuf];
 
@@ -531,15 +535,15 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
   // fragment offsets within a buffer: K for step ds (key block 0; block 1 is 32 rows on),
-  // V^T for step ks, low/high unit (dim block 0; block db is 32 db rows on)
+  // V^T of dim block 0 for unit 4 k + 2 hi + hl (block db: 32 db rows on, at the unit
+  // XOR 2 db, i.e. k ^ db / 2 and hi ^ db % 2)
   int ko[8], vo[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) ko[ds] = koff(l32, 2 * ds + hl);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    vo[2 * ks] = kKBytes + voff(l32, 4 * ks + hl);
-    vo[2 * ks + 1] = kKBytes + voff(l32, 4 * ks + 2 + hl);
-  }
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) vo[2 * k + hi] = kKBytes + voff(l32, 4 * k + 2 * hi + hl);
 
   // Tile loads. Key rows past kvalid - 1 re-read that row: those keys come after every
   // query of the call, so their scores are masked and their probabilities are exactly 0.
@@ -555,6 +559,7 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   uint2 vr[VT][4][VW];  // task i, key kk: VD dims as 8-byte words
   auto load_v = [&](int k0) {
+    if (!v_task) return;
 #pragma unroll
     for (int i = 0; i < VT; ++i) {
       const int task = (int)threadIdx.x + i * NT;
@@ -574,6 +579,7 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   // V^T row d = VD dq + j, unit q4: keys 4 q4 .. +3 of dim d, packed two keys a word
   auto store_v = [&](char* buf) {
+    if (!v_task) return;
     char* vt = buf + kKBytes;
 #pragma unroll
     for (int i = 0; i < VT; ++i) {
@@ -677,8 +683,8 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(buf + vo[2 * ks] + db * 32 * kVRow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(buf + vo[2 * ks + 1] + db * 32 * kVRow);
+        const uint2 lo = *reinterpret_cast<const uint2*>(buf + vo[2 * (ks ^ (db >> 1)) + (db & 1)] + db * 32 * kVRow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(buf + vo[2 * (ks ^ (db >> 1)) + (1 ^ (db & 1))] + db * 32 * kVRow);
         o[db] = mma(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[ks], o[db]);
       }
     if (more) {
