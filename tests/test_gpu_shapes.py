@@ -44,6 +44,12 @@ SHAPES = [
                               num_experts=5, moe_intermediate_size=320, seq=70, batch=1)),
     ("fp32_d128_g2", dict(act_dtype="f32", hidden_size=256, num_heads=4, num_kv_heads=2, head_dim=128, rope_dim=64,
                           num_experts=2, moe_intermediate_size=256, seq=17, batch=2, temp_range=(1.0, 1.0))),
+    # bf16 head_dim 128 with 2 and 1 query heads per key head, long enough (25 key tiles)
+    # that the longest query tiles split over key chunks and are merged
+    ("d128_g2_split", dict(hidden_size=512, num_heads=4, num_kv_heads=2, head_dim=128, rope_dim=64,
+                           num_experts=4, moe_intermediate_size=128, seq=1600, batch=1)),
+    ("d128_g1_split", dict(hidden_size=256, num_heads=2, num_kv_heads=2, head_dim=128, rope_dim=64,
+                           num_experts=3, moe_intermediate_size=128, seq=1550, batch=1)),
 ]
 
 
