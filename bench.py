@@ -330,11 +330,16 @@ def cpu_baseline(cfg):
     inp = block_inputs(cfg)
     x = inp["x"].numpy().astype(np.float64)
     s = inp["s_in"].float().numpy()
-    t0 = time.perf_counter()
-    O.block_forward(cfg, w, x, s, None)
-    dt = time.perf_counter() - t0
-    return {"value": round(cfg.tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full prefill of the {cfg.seq}-token workload (batch {cfg.batch}) in {dt:.1f} s"}
+    # whole prefills of the workload, repeated until about 10 s of host time have passed
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        O.block_forward(cfg, w, x, s, None)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0:
+            break
+    return {"value": round(runs * cfg.tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} full prefill(s) of the {cfg.seq}-token workload (batch {cfg.batch}) in {dt:.1f} s"}
 
 
 # ----------------------------------------------------------------------------- main

@@ -319,9 +319,9 @@ static hipError_t launch_down_cfg(const MoeArgs<T>& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Row tile by load: 16-row tiles when experts see only a few tokens each (decode);
-// otherwise 128-row tiles for gate/up and 64-row tiles for down (its K is the expert
-// width and its column tiles few, so smaller row tiles keep every CU busy).
+// Row tile by load: 16-row tiles when experts see only a few tokens each (decode), with
+// 64 output columns per item for down so its items (about twice the CU count) fill the
+// chip; otherwise 128 x 128 tiles.
 template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
@@ -332,7 +332,7 @@ hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s) {
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
-  if (a.ntok <= 32 * a.E) return launch_down_cfg<T, 16, 1, 4>(a, s);
+  if (a.ntok <= 32 * a.E) return launch_down_cfg<T, 16, 1, 4, 64>(a, s);
   return launch_down_cfg<T, 128, 2, 2>(a, s);
 }
 
