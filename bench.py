@@ -230,18 +230,19 @@ def time_steps(setup: Setup, steps: int, warmup: int, hip: _Hip):
         setup.step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
-    e0, e1 = hip.event(), hip.event()
+    evs = [hip.event() for _ in range(steps + 1)]  # one between every two steps: median and minimum
     t0 = time.perf_counter()
-    hip.record(e0, stream)
-    for _ in range(steps):
+    hip.record(evs[0], stream)
+    for k in range(steps):
         setup.step()
-    hip.record(e1, stream)
+        hip.record(evs[k + 1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = hip.elapsed(e0, e1) / steps
-    hip.destroy(e0)
-    hip.destroy(e1)
-    return ms, wall
+    ms = hip.elapsed(evs[0], evs[-1]) / steps
+    per = [hip.elapsed(evs[k], evs[k + 1]) for k in range(steps)]
+    for e in evs:
+        hip.destroy(e)
+    return ms, wall, float(np.median(per)), float(min(per))
 
 
 def time_graph(setup: Setup, steps: int, warmup: int, hip: _Hip):
@@ -294,7 +295,7 @@ def time_stages(setup: Setup, steps: int, hip: _Hip):
 def measure(cfg, steps, warmup, hip):
     setup = Setup(cfg)
     n_routed, n_used, counts = setup.routing()
-    ms, wall = time_steps(setup, steps, warmup, hip)
+    ms, wall, ms_med, ms_min = time_steps(setup, steps, warmup, hip)
     graph_ms = time_graph(setup, steps, warmup, hip) if cfg.decode else None
     stages = time_stages(setup, steps, hip)
     work = stage_work(cfg, n_routed, n_used)
@@ -312,14 +313,34 @@ def measure(cfg, steps, warmup, hip):
     total_b = sum(v[1] for v in work.values())
     del setup
     torch.cuda.empty_cache()
-    return {"ms": ms, "graph_ms": graph_ms, "wall": wall, "stages": table, "roofline": roof, "n_routed": n_routed, "experts_used": n_used,
+    return {"ms": ms, "ms_median": ms_med, "ms_min": ms_min, "graph_ms": graph_ms, "wall": wall, "stages": table, "roofline": roof, "n_routed": n_routed, "experts_used": n_used,
             "expert_counts": counts, "step_gflop": total_f / 1e9, "step_mbytes": total_b / 1e6}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_name() -> str:
+    try:
+        return str(np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"])
+    except Exception:  # pragma: no cover
+        return "unknown"
+
+
 def cpu_baseline(cfg):
-    """The CPU oracle (as it stands) on the same seeded prefill input, timed on the host."""
+    """The CPU oracle (as it stands) on the same seeded prefill input, timed on the host:
+    whole prefills repeated until about 10 s have passed (at least three when they fit);
+    the value comes from the median run."""
     from oracle import zaya_oracle as O
     try:
         import threadpoolctl
@@ -330,16 +351,72 @@ def cpu_baseline(cfg):
     inp = block_inputs(cfg)
     x = inp["x"].numpy().astype(np.float64)
     s = inp["s_in"].float().numpy()
-    # whole prefills of the workload, repeated until about 10 s of host time have passed
-    runs, t0 = 0, time.perf_counter()
+    runs = []
+    t_all = time.perf_counter()
     while True:
+        t0 = time.perf_counter()
         O.block_forward(cfg, w, x, s, None)
-        runs += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0:
+        runs.append(time.perf_counter() - t0)
+        spent = time.perf_counter() - t_all
+        if spent >= 10.0 and (len(runs) >= 3 or spent >= 20.0):
             break
-    return {"value": round(runs * cfg.tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} full prefill(s) of the {cfg.seq}-token workload (batch {cfg.batch}) in {dt:.1f} s"}
+    med = float(np.median(runs))
+    return {"value": round(cfg.tokens / med, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(runs)} full prefills of the {cfg.seq}-token workload (batch {cfg.batch}) in "
+                      f"{sum(runs):.1f} s; median {med:.2f} s, min {min(runs):.2f} s per prefill",
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(), "blas": _blas_name()}
+
+
+# ----------------------------------------------------------------------------- ceilings
+
+def measure_ceilings(hip):
+    """Attainable ceilings of this device beside the published peaks: the library's HBM
+    read probe, a plain 1 GiB device-to-device copy (read + write) and the library's
+    matrix-core probe (bf16 32x32x16 MFMAs on register operands). Best of five each."""
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            fn()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            out.append(hip.elapsed(e0, e1))
+            hip.destroy(e0)
+            hip.destroy(e1)
+        return min(out)
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = best_ms(lambda: dst.copy_(src))
+    copy_gbs = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    buf = torch.zeros(1 << 31, dtype=torch.uint8, device="cuda")  # 2 GiB, read once per run
+    rsink = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    read_ms = best_ms(lambda: Z.zaya_probe_hbm_read(buf.data_ptr(), buf.numel(), 2048, rsink.data_ptr(), stream))
+    read_gbs = buf.numel() / (read_ms * 1e-3) / 1e9
+    del buf, rsink
+    n_wg, iters = 256 * 8, 2000
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    flops = [0.0]
+
+    def probe():
+        flops[0] = Z.zaya_probe_mfma_bf16(n_wg, iters, sink.data_ptr(), stream)
+
+    mfma_ms = best_ms(probe)
+    del sink
+    torch.cuda.empty_cache()
+    return {"hbm_gbs": {"spec": PEAK_HBM_GBS, "measured": round(read_gbs, 1),
+                        "probe": "2 GiB read once with non-temporal 16-byte loads (2048 workgroups), best of 5"},
+            "hbm_copy_gbs": {"spec": PEAK_HBM_GBS, "measured": round(copy_gbs, 1),
+                             "probe": "1 GiB fp32 device-to-device copy, read + write bytes / time, best of 5"},
+            "mfma_bf16_tflops": {"spec": PEAK_BF16_TFLOPS, "measured": round(flops[0] / (mfma_ms * 1e-3) / 1e12, 1),
+                                 "probe": f"{n_wg} workgroups x 4 waves x {iters} rounds of 8 independent "
+                                          "32x32x16 bf16 MFMAs on varied register operands, best of 5"}}
 
 
 # ----------------------------------------------------------------------------- main
@@ -370,6 +447,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    ceil = None if args.copy_calibration else measure_ceilings(hip)
     pcfg = CONFIGS["prefill"]
     pre = measure(pcfg, args.steps, args.warmup, hip)
     print(f"[bench] prefill {pre['ms']:.4f} ms/step", file=sys.stderr, flush=True)
@@ -400,7 +478,9 @@ def main():
                    "seq_len": pcfg.seq, "parallelism": "single GPU"},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
-        "prefill": {"tok_s": round(value, 1), "step_gflop": round(pre["step_gflop"], 2),
+        "ceilings": ceil,
+        "prefill": {"tok_s": round(value, 1), "ms_median": round(pre["ms_median"], 5), "ms_min": round(pre["ms_min"], 5),
+                    "step_gflop": round(pre["step_gflop"], 2),
                     "frac_of_mfma_peak": round(pre["step_gflop"] / (pre["ms"] * 1e-3) / 1e3 / PEAK_BF16_TFLOPS, 4),
                     "routed_tokens": pre["n_routed"], "experts_used": pre["experts_used"], "stages": pre["stages"],
                     "wall_s": round(pre["wall"], 4)},
@@ -408,6 +488,7 @@ def main():
     if dec is not None:
         dcfg = CONFIGS["decode"]
         line["decode"] = {"tok_s": round(dcfg.batch / (dec["ms"] * 1e-3), 1), "ms_per_step": round(dec["ms"], 5),
+                          "ms_median": round(dec["ms_median"], 5), "ms_min": round(dec["ms_min"], 5),
                           "step_mbytes": round(dec["step_mbytes"], 1),
                           "frac_of_hbm_peak": round(dec["step_mbytes"] / (dec["ms"] * 1e-3) / 1e3 / PEAK_HBM_GBS, 4),
                           "experts_used": dec["experts_used"], "roofline": dec["roofline"], "stages": dec["stages"],
@@ -424,6 +505,10 @@ def main():
         c2 = CONFIGS["prefill_conv2"]
         line["prefill_two_stage_conv"] = {"tok_s": round(c2.tokens / (pre2["ms"] * 1e-3), 1),
                                           "ms_per_step": round(pre2["ms"], 5), "cca": pre2["stages"]["cca"]}
+    if ceil is not None:  # the dominant kernels also against the measured ceilings
+        for r in [line["roofline"]] + ([line["decode"]["roofline"]] if "decode" in line else []):
+            ref = ceil["hbm_gbs"]["measured"] if r["unit"] == "GB/s" else ceil["mfma_bf16_tflops"]["measured"]
+            r["frac_of_measured"] = round(r["achieved"] / ref, 4) if ref > 0 else None
     print(json.dumps(line))
 
 

@@ -272,6 +272,23 @@ int zaya_set_stage_events(void* const* events, int n);
 /* Name of stage k (0 <= k < ZAYA_N_STAGES), or "" out of range. */
 const char* zaya_stage_name(int k);
 
+/* Benchmark probe of the matrix cores (not needed for correct use): enqueues n_wg
+ * workgroups of 256 threads on `stream`; each wave runs `iters` rounds of eight
+ * independent 32x32x16 bf16 MFMAs on register operands (no memory traffic in the
+ * loop) and writes one float per thread to sink[0 .. 256 n_wg) (device memory, owned by
+ * the caller). *flops (host pointer, may be NULL) receives the dense flops the launch
+ * performs, so flops / elapsed time is the attainable bf16 MFMA rate. Returns
+ * ZAYA_EINVAL if n_wg <= 0, iters <= 0 or sink is NULL, ZAYA_EHIP if the launch fails. */
+int zaya_probe_mfma_bf16(int n_wg, int iters, float* sink, void* stream, double* flops);
+
+/* Benchmark probe of HBM reads (not needed for correct use): enqueues n_wg workgroups
+ * of 256 threads on `stream` that read every byte of src[0 .. bytes) (device memory,
+ * 16-byte aligned, bytes a multiple of 16) once with non-temporal 16-byte loads and
+ * write one float per thread to sink[0 .. 256 n_wg) (device memory). bytes / elapsed
+ * time is the attainable read rate. Returns ZAYA_EINVAL on a NULL pointer, n_wg <= 0,
+ * or a misaligned or short buffer, ZAYA_EHIP if the launch fails. */
+int zaya_probe_hbm_read(const void* src, size_t bytes, int n_wg, float* sink, void* stream);
+
 /* Message of the calling thread's last failed call ("" if none). */
 const char* zaya_last_error(void);
 /* Name of a status code. */

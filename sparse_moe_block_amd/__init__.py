@@ -107,6 +107,10 @@ def lib():
         L.zaya_set_stage_events.restype = i
         L.zaya_stage_name.argtypes = [i]
         L.zaya_stage_name.restype = C.c_char_p
+        L.zaya_probe_mfma_bf16.argtypes = [i, i, vp, vp, C.POINTER(C.c_double)]
+        L.zaya_probe_mfma_bf16.restype = i
+        L.zaya_probe_hbm_read.argtypes = [vp, sz, i, vp, vp]
+        L.zaya_probe_hbm_read.restype = i
         _lib = L
     return _lib
 
@@ -259,10 +263,23 @@ def zaya_stage_name(k: int) -> str:
     return lib().zaya_stage_name(k).decode()
 
 
+def zaya_probe_mfma_bf16(n_wg: int, iters: int, sink_ptr: int, stream: int) -> float:
+    """Enqueue the matrix-core probe (see include/zaya.h); returns the flops it performs."""
+    flops = C.c_double(0.0)
+    _check(lib().zaya_probe_mfma_bf16(n_wg, iters, C.c_void_p(sink_ptr), C.c_void_p(stream), C.byref(flops)))
+    return float(flops.value)
+
+
+def zaya_probe_hbm_read(src_ptr: int, nbytes: int, n_wg: int, sink_ptr: int, stream: int) -> None:
+    """Enqueue the HBM read probe (see include/zaya.h)."""
+    _check(lib().zaya_probe_hbm_read(C.c_void_p(src_ptr), nbytes, n_wg, C.c_void_p(sink_ptr), C.c_void_p(stream)))
+
+
 def abi_version() -> int:
     return int(lib().zaya_abi_version())
 
 
 __all__ = ["zaya_block_prefill", "zaya_block_decode", "zaya_stack_forward", "zaya_block_workspace_bytes",
            "zaya_stack_workspace_bytes", "ZayaError", "ZayaLibraryMissing", "lib", "abi_version", "LIB_PATH",
-           "TAP_FIELDS", "WEIGHT_FIELDS", "zaya_set_stage_events", "zaya_stage_name", "N_STAGES"]
+           "TAP_FIELDS", "WEIGHT_FIELDS", "zaya_set_stage_events", "zaya_stage_name", "N_STAGES",
+           "zaya_probe_mfma_bf16", "zaya_probe_hbm_read"]
