@@ -262,3 +262,14 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(Z, "_lib", None)
     with pytest.raises(Z.ZayaLibraryMissing):
         Z.zaya_block_workspace_bytes(CONFIGS["tiny"], 1, 8)
+
+
+def test_probe_arguments_are_checked(L):
+    flops = C.c_double(0.0)
+    assert L.zaya_probe_mfma_bf16(0, 10, C.c_void_p(FAKE), None, C.byref(flops)) == -1
+    assert L.zaya_probe_mfma_bf16(4, 0, C.c_void_p(FAKE), None, C.byref(flops)) == -1
+    assert L.zaya_probe_mfma_bf16(4, 10, None, None, C.byref(flops)) == -1
+    assert L.zaya_probe_hbm_read(C.c_void_p(FAKE), 4096, 0, C.c_void_p(FAKE), None) == -1
+    assert L.zaya_probe_hbm_read(C.c_void_p(FAKE + 8), 4096, 4, C.c_void_p(FAKE), None) == -1  # misaligned
+    assert L.zaya_probe_hbm_read(C.c_void_p(FAKE), 4100, 4, C.c_void_p(FAKE), None) == -1  # not 16-byte whole
+    assert L.zaya_probe_hbm_read(None, 4096, 4, C.c_void_p(FAKE), None) == -1
