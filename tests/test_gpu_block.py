@@ -114,6 +114,14 @@ def test_full_prefill_workload_sampled_rows():
     _full_check(cfg, rows=_sample_rows(cfg.tokens))
 
 
+def test_full_prefill_two_stage_conv_sampled_rows():
+    """The benchmark's prefill workload with the printout's two-stage conv (depthwise k2,
+    then grouped k2 per head), batch 1 x 4096 tokens at full widths, in the launch
+    configuration the benchmark times: every tap on sampled rows, routing bit-exact."""
+    cfg = CONFIGS["prefill_conv2"]
+    _full_check(cfg, rows=_sample_rows(cfg.tokens))
+
+
 def test_full_decode_workload():
     """The benchmark's decode workload: batch 64, one new token each over 8192 cached."""
     _full_check(CONFIGS["decode"])
