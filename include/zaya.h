@@ -156,7 +156,16 @@ typedef struct zaya_block_weights {
  * slots whatever the sequence length. It needs sliding_window >= 0 and cap >=
  * sliding_window + 1; cache_len may then exceed cap. A prefill (S > 1) into a ring
  * needs fresh sequences (every cache_len[b] == 0): the chunk's keys are formed in the
- * workspace and the last min(S, cap) positions stored. */
+ * workspace and the last min(S, cap) positions stored.
+ * Host and device lengths: validation and a few launch sizes come from the host array,
+ * the kernels read cache_len_dev. A call captured in a HIP graph and replayed after the
+ * caller advanced cache_len_dev (not the host array, which a graph cannot see) is
+ * valid for zaya_block_decode as long as every device length stays below cap (linear
+ * cache; a ring has no limit): the decode attention derives each sequence's key chunks
+ * from its device length and the step always forms the delayed value. A position at or
+ * past cap of a linear cache is never written (nor read), so exceeding it drops keys
+ * instead of faulting. zaya_block_prefill takes its attention split from the host
+ * lengths: a captured prefill is valid only for the lengths it was captured with. */
 typedef struct zaya_cca_cache {
   void* K;
   void* V;
@@ -231,7 +240,7 @@ int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w,
 typedef struct zaya_stack_config {
   zaya_block_config block;
   int n_layers;
-  int vocab;
+  int vocab;  /* a multiple of 4 (the head stores four logits per lane), else ZAYA_ESHAPE */
   /* Which blocks use block.sliding_window (the 74B preview's hybrid_sliding blocks are
    * every other block, same page and section as the ring above): 0 = all of them; 1 =
    * blocks 0, 2, 4, ... (the others attend to the whole prefix); 2 = blocks 1, 3, 5, ... */

@@ -184,7 +184,7 @@ def causal_conv3(cin, hist, cw, cb):
     return y, ext
 
 
-def causal_conv_two_stage(cin, x_prev, y1_prev, w1, b1, w2, b2, groups, rnd):
+def causal_conv_two_stage(cin, x_prev, y1_prev, w1, b1, w2, b2, groups, rnd, trace=None):
     """The printout's two causal convolutions over the q/k channels, one sequence.
 
     ("Printout": conv_qk_depthwise = Conv1d(C, C, kernel 2, groups C) and
@@ -197,13 +197,16 @@ def causal_conv_two_stage(cin, x_prev, y1_prev, w1, b1, w2, b2, groups, rnd):
     (output channel, tap, input channel of its group), b2 [C]. Tap 0 takes the previous
     token, tap 1 the current one. Reading: each convolution's output is rounded to the
     act dtype (separate modules); the two-slot state holds (x_{t-1}, y1_{t-1}).
-    Returns y2 [S, C] and the new state (x_{S-1}, y1_{S-1}).
+    Returns y2 [S, C] and the new state (x_{S-1}, y1_{S-1}). trace: optional dict that
+    receives the depthwise outputs y1 of rows t = -1 .. S-1 (for error analysis only).
     """
     S, C = cin.shape
     x = np.concatenate([f64(x_prev)[None], f64(cin)], axis=0)  # rows t = -1 .. S-1
     w1 = f64(w1)
     y1 = rnd(f64(b1)[None] + w1[:, 0][None] * x[0:S] + w1[:, 1][None] * x[1:S + 1])
     y1e = np.concatenate([f64(y1_prev)[None], y1], axis=0)  # rows t = -1 .. S-1
+    if trace is not None:
+        trace["y1"] = y1e
     gs = C // groups
     y2 = np.empty((S, C))
     w2 = f64(w2)
@@ -233,7 +236,7 @@ def rope_rotate(x, pos, rope_dim, theta):
     return x
 
 
-def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd):
+def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd, trace=None):
     """Queries, keys and values of the CCA projection for B sequences.
 
     xn: [B, S, H] normed input (act values). cache_len: [B] ints. conv_state:
@@ -252,6 +255,9 @@ def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd):
       5. rotary on the first rope_dim dims; round to act;
       6. value head g = [current half of token t ‖ delayed half of token t-1].
     Returns Q [B, nh, S, d], K [B, nkv, S, d], V [B, nkv, S, d] and the new states.
+    trace: optional dict that receives, per sequence, the convolution's inputs (history
+    rows first), its outputs, the depthwise outputs of the two-stage form and the
+    pre-norm query and key vectors (for error analysis only; nothing else changes).
     """
     B, S, H = xn.shape
     nh, nkv, d, r = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.rope_dim
@@ -276,9 +282,10 @@ def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd):
         fresh = int(cache_len[b]) == 0
         hist = np.zeros((2, C)) if fresh else f64(conv_state[b]).T  # [2, C]
         cin = np.concatenate([Pq[b].reshape(S, nh * d), Pk[b].reshape(S, nkv * d)], axis=1)
+        tb = {} if trace is not None else None
         if cfg.conv_k == 2:  # the printout's two kernel-2 convolutions; state = (x_{t-1}, y1_{t-1})
             y, xl, y1l = causal_conv_two_stage(cin, hist[0], hist[1], w["conv_w"], w["conv_b"], w["conv2_w"],
-                                               w["conv2_b"], nh + nkv, rnd)
+                                               w["conv2_b"], nh + nkv, rnd, trace=tb)
             ext = np.concatenate([np.zeros((S, C)), xl[None], y1l[None]], axis=0)  # new state rows S, S+1
         else:
             y, ext = causal_conv3(cin, hist, w["conv_w"], w["conv_b"])
@@ -293,6 +300,9 @@ def cca_project(cfg, w, xn, cache_len, conv_state, prev_hs, rnd):
             rk[:, g] = np.mean(rq[:, g * G:(g + 1) * G], axis=1)
         qt = yq + rq
         kt = yk + rk
+        if trace is not None:
+            tb.update(hist=hist, cin=cin, conv=y, qt=qt, kt=kt)
+            trace.setdefault("seq", []).append(tb)
         # L2 norm to sqrt(d); keys scaled by temp (reading: norm clamped at 1e-12)
         qn = math.sqrt(d) * qt / np.maximum(np.linalg.norm(qt, axis=-1, keepdims=True), 1e-12)
         kn = math.sqrt(d) * kt / np.maximum(np.linalg.norm(kt, axis=-1, keepdims=True), 1e-12)

@@ -748,8 +748,7 @@ constexpr int kDecChunkMin = 256;   // keys per decode chunk, at least
 constexpr int kDecChunksMax = 128;  // chunks per (sequence, KV group), at most
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, float* __restrict__ part, int nchunk,
-                                                             int chunk) {
+__global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, float* __restrict__ part, int nchunk) {
   constexpr int NT = 64 * G;
   constexpr int KROW = D * (int)sizeof(T) + 16;
   constexpr int VROW = D * (int)sizeof(T) + 16;
@@ -769,11 +768,16 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
   const int h = g * G + wave;
   const int L0 = cached_len(a.cache_len, b);
   const int qp = L0;  // the new token's position
-  const int kvalid = L0 + 1;
+  // a linear cache holds positions below cap only (a position past it was not stored)
+  const int kvalid = a.ring ? L0 + 1 : min(L0 + 1, a.cap);
   const int W = a.window;
   const int klo = W >= 0 ? max(0, qp - W) : 0;
-  // chunks tile the visible range from the 64-aligned position at or below its start
+  // the nchunk chunks of this sequence tile its visible range from the 64-aligned
+  // position at or below its start; the chunk length follows from the sequence's own
+  // cache length on the device, so the grid covers every key whatever that length is
   const int kbase = (klo / 64) * 64;
+  const int span = max(kvalid - kbase, 1);
+  const int chunk = ((span + nchunk - 1) / nchunk + 63) / 64 * 64;
   const int c_lo = max(klo, kbase + c * chunk), c_hi = min(kvalid, kbase + (c + 1) * chunk);
   const float sscale = kLog2e / sqrtf((float)D);
 
@@ -888,6 +892,18 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
           o[1] = dot2_bf16(pp[kk], __builtin_amdgcn_perm(v1, v0, 0x07060302u), o[1]);  // high halves
         }
       }
+    } else if constexpr (kDot2) {
+      // head_dim 64: one dim per lane, two keys per product (v_k[lane], v_k+1[lane])
+#pragma unroll 4
+      for (int k = 0; k < 64; k += 8) {
+        const u32x4 pp = *reinterpret_cast<const u32x4*>(&p2_s[wave][k / 2]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vt_s + (k + 2 * kk) * VROW + lane * 2);
+          const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vt_s + (k + 2 * kk + 1) * VROW + lane * 2);
+          o[0] = dot2_bf16(pp[kk], v0 | (v1 << 16), o[0]);
+        }
+      }
     } else {
       // four keys per step
 #pragma unroll 4
@@ -982,11 +998,13 @@ static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, h
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_dg(const AttnArgs<T>& a, float* part, int span, hipStream_t s) {
+  // chunk count from the host's largest span; each sequence's chunk length is derived
+  // on the device (the kernel), so a call replayed with grown cache lengths (a captured
+  // graph) still visits every key, in fewer, longer chunks
   int nchunk = min(kDecChunksMax, (span + kDecChunkMin - 1) / kDecChunkMin);
   const int chunk = (((span + nchunk - 1) / nchunk) + 63) / 64 * 64;
   nchunk = (span + chunk - 1) / chunk;
-  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), dim3(nchunk, a.nkv, a.B), dim3(64 * G), 0, s, a, part, nchunk,
-                     chunk);
+  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), dim3(nchunk, a.nkv, a.B), dim3(64 * G), 0, s, a, part, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine_kernel<T, D, G>), dim3(a.B * a.nh), dim3(64), 0, s, a, part, nchunk);

@@ -287,6 +287,9 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         const int sl = i / cps, q = i % cps, rw = q / cpr, ch = q % cpr;
         const int t2 = base + sl;
         if (t2 >= t_end) continue;
+        // a linear cache stores positions below cap only (the host checks cache_len + S
+        // <= cap; a replayed call with grown device lengths must not write past it)
+        if (rw >= G && !a.ring && L0 + t2 >= a.cap) continue;
         const u32x4 val = *reinterpret_cast<const u32x4*>(outs + ((wave * tpw + sl) * (G + 2) + rw) * d + ch * E16);
         const size_t pos2 = a.ring ? (size_t)((L0 + t2) % a.cap) : (size_t)(L0 + t2);  // cache slot
         T* dst;

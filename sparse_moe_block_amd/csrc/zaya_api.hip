@@ -198,6 +198,10 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   const int32_t* cl_dev;
   bool any_cached = false;
   if (cache) {
+    // decode always forms the delayed value of the token before the step (the kernels
+    // ignore it for fresh sequences), so a captured decode step stays valid when the
+    // device-side lengths grow from zero
+    any_cached = decode;
     for (int b = 0; b < B; ++b) any_cached |= cache->cache_len[b] > 0;
     if (cache->cache_len_dev) {
       cl_dev = cache->cache_len_dev;
@@ -446,7 +450,8 @@ int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w,
 }
 
 size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S) {
-  if (!cfg || check_config(&cfg->block) || B <= 0 || S <= 0 || cfg->window_layers < 0 || cfg->window_layers > 2)
+  if (!cfg || check_config(&cfg->block) || B <= 0 || S <= 0 || cfg->window_layers < 0 || cfg->window_layers > 2 ||
+      cfg->n_layers <= 0 || cfg->vocab <= 0 || cfg->vocab % 4)
     return 0;
   return plan_stack(cfg, B, S).total;
 }
@@ -459,6 +464,8 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
   int rc = check_config(&cfg->block);
   if (rc) return rc;
   if (cfg->n_layers <= 0 || cfg->vocab <= 0) return fail(ZAYA_ESHAPE, "n_layers %d vocab %d", cfg->n_layers, cfg->vocab);
+  // the lm_head GEMM stores four logits per lane: rows must hold whole, aligned groups
+  if (cfg->vocab % 4) return fail(ZAYA_ESHAPE, "vocab %d must be a multiple of 4", cfg->vocab);
   if (!w || !w->embed || !w->emb_shift || !w->emb_scale || !w->final_g || !w->blocks)
     return fail(ZAYA_EINVAL, "stack weights incomplete");
   for (int l = 0; l < cfg->n_layers; ++l)

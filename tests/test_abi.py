@@ -246,6 +246,13 @@ def test_stack_validation(L):
     assert call(sc) == -4  # everything else valid: the empty workspace is what stops it
     bad = Z.StackConfig(Z.block_config(cfg.replace(head_dim=80)), cfg.num_layers, cfg.vocab_size)
     assert call(bad) == -2
+    # the head stores four logits per lane: a vocabulary that is not a multiple of 4 is
+    # rejected before any launch (and has no workspace size)
+    for v in (262145, 1002, 3):
+        assert call(Z.StackConfig(Z.block_config(cfg), cfg.num_layers, v)) == -2
+        assert "multiple of 4" in L.zaya_last_error().decode()
+        assert Z.zaya_stack_workspace_bytes(cfg.replace(vocab_size=v), 4, 16) == 0
+    assert Z.zaya_stack_workspace_bytes(cfg.replace(vocab_size=262272), 4, 16) > 0
     # hybrid stacks: window_layers in {0, 1, 2}
     assert call(Z.StackConfig(Z.block_config(cfg.replace(sliding_window=64)), cfg.num_layers, cfg.vocab_size, 1)) == -4
     bad = Z.StackConfig(Z.block_config(cfg), cfg.num_layers, cfg.vocab_size, 3)
@@ -273,3 +280,4 @@ def test_probe_arguments_are_checked(L):
     assert L.zaya_probe_hbm_read(C.c_void_p(FAKE + 8), 4096, 4, C.c_void_p(FAKE), None) == -1  # misaligned
     assert L.zaya_probe_hbm_read(C.c_void_p(FAKE), 4100, 4, C.c_void_p(FAKE), None) == -1  # not 16-byte whole
     assert L.zaya_probe_hbm_read(None, 4096, 4, C.c_void_p(FAKE), None) == -1
+

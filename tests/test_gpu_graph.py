@@ -102,3 +102,56 @@ def test_graph_captured_decode_step_is_bit_identical_to_eager():
                                got[k].view(torch.uint8) if v.dtype != torch.float32 else got[k].view(torch.int32)), \
                 f"replay {rep}: {k} differs from the eager step"
         print(f"replay {rep}: {len(eager)} tensors bit-identical", flush=True)
+
+
+def test_graph_replay_with_grown_cache_length_matches_oracle():
+    """A decode step captured at cache length 1000 and replayed after the caller advanced
+    the device-side lengths to 1100 (a graph cannot see the host array): the attention
+    covered 4 chunks of 256 keys (1024 positions) at capture, so the replay must derive
+    longer chunks from the device lengths to reach all 1101 keys. Checked against the
+    oracle's decode at length 1100 (routing teacher-forced to the replay's, R1 bit-exact)."""
+    import numpy as np
+    from oracle import zaya_oracle as O
+    from tests.zaya_harness import compare, np_weights, stream_bound, to_np, upload_weights
+    from zaya_synth import block_inputs, block_weights
+    L_new, L_cap = 1100, 1000
+    cfg = CONFIGS["decode"].replace(name="decode_graph_grow", batch=4, kv_len=L_new)
+    B, H, R, E = cfg.batch, cfg.hidden_size, cfg.router_hidden, cfg.num_experts
+    w_host = block_weights(cfg)
+    inp = block_inputs(cfg)  # K/V filled to 1100 positions, cap 1101
+    w = upload_weights(w_host)
+    cache = {k: inp[k].to(DEV).contiguous() for k in ("K", "V", "conv_state", "prev_hs")}
+    cache["cache_len"] = [L_cap] * B
+    cache["cache_len_dev"] = torch.full((B,), L_cap, dtype=torch.int32, device=DEV)
+    x, s_in = inp["x"].to(DEV), inp["s_in"].to(DEV)
+    xo = torch.full((B, 1, H), float("nan"), device=DEV)
+    so = torch.full((B, 1, R), float("nan"), device=DEV, dtype=cfg.torch_dtype)
+    taps = {"router_logits": torch.full((B, 1, E + 1), float("nan"), device=DEV, dtype=cfg.torch_dtype),
+            "expert_classes": torch.full((B, 1), -7, device=DEV, dtype=torch.int32)}
+    ws = torch.empty(Z.zaya_block_workspace_bytes(cfg, B, 1, True), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    print(f"[gpu] capture decode at cache length {L_cap}, replay at {L_new}", flush=True)
+    with torch.cuda.graph(graph):  # capture only: nothing runs until the replay
+        Z.zaya_block_decode(cfg, w, B, x, s_in, xo, so, cache, taps, ws)
+    torch.cuda.synchronize()
+    cache["cache_len_dev"].fill_(L_new)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    npw = np_weights(w_host)
+    gcls = taps["expert_classes"].cpu().numpy().reshape(-1)
+    lg = to_np(taps["router_logits"]).reshape(B, E + 1)
+    cls, _, _ = O.select(lg, npw["bal_bias"].astype(np.float64), O.rnd_bf16)
+    assert np.array_equal(cls, gcls)
+    ocache = {k: inp[k].float().numpy() for k in ("K", "V", "conv_state", "prev_hs")}
+    ocache["cache_len"] = np.full(B, L_new)
+    ref = O.block_forward(cfg, npw, inp["x"].numpy().astype(np.float64), inp["s_in"].float().numpy(), ocache,
+                          force_cls=gcls)
+    r = compare("layer_output", to_np(xo).reshape(B, H), ref["layer_output"], "bf16",
+                bound=stream_bound("bf16", ref["attention_output"], ref["layer_output"], ref["mlp_output"],
+                                   npw["m_rs"]))
+    compare("router_state", to_np(so).reshape(B, R), ref["router_state"], "bf16")
+    compare("new key at 1100", to_np(cache["K"][:, :, L_new]), ref["attention_keys"][:, :, 0], "bf16")
+    compare("conv_state", to_np(cache["conv_state"]), ref["conv_state"], "bf16")
+    print("replay at grown cache length:", r, flush=True)

@@ -70,3 +70,14 @@ def test_decode_mixed_cache_lengths():
 def test_windowed_prefill_after_cache():
     cfg = CONFIGS["prefill"].replace(name="prefill_win_cached", batch=2, seq=77, kv_len=130, sliding_window=50)
     _check(cfg)
+
+
+# Decode in bf16 at head_dim 64 (one dim per lane in the weighted sum, keys paired for
+# the bf16 dot products), with 1 and 4 query heads per key head and cache lengths of
+# mixed sizes, including a fresh sequence and a partial last tile.
+@pytest.mark.parametrize("G", [1, 4])
+def test_decode_bf16_head_dim_64(G):
+    cfg = _small(name=f"decode_d64_g{G}", hidden_size=512, num_heads=4, num_kv_heads=4 // G, head_dim=64,
+                 rope_dim=32, num_experts=6,
+                 moe_intermediate_size=128, batch=5, seq=1, kv_len=300, decode=True)
+    _check(cfg, lens=[0, 1, 64, 129, 300])
