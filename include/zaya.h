@@ -233,6 +233,26 @@ int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w,
                       const zaya_cca_cache* cache, const zaya_taps* taps, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Allocation-free decode step, for callers that cannot allocate device memory or hand
+ * the library a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments and contract as zaya_block_decode without the
+ * workspace: the intermediates live in a static device array of
+ * ZAYA_NOALLOC_SCRATCH_BYTES bytes (64 MiB: a decode step of 64 sequences at the
+ * ZAYA1-8B widths needs about 43 MiB) that each device the library runs on holds from
+ * the first call on it until the process ends. Call with the stream's device current.
+ * Returns ZAYA_EWORKSPACE, with nothing launched, when the step needs more than the
+ * array (zaya_block_workspace_bytes(cfg, B, 1, 1) > ZAYA_NOALLOC_SCRATCH_BYTES), and
+ * ZAYA_EHIP if the array's device address cannot be obtained. Makes no hipMalloc,
+ * hipFree or other allocating call. Every call on one device shares that device's array,
+ * which keeps the last call's contents (no kernel reads a byte of it before writing it
+ * in the same call, so nothing needs clearing): calls that overlap on one device (two
+ * streams, or two threads) race, and the caller must serialise them. Under graph
+ * capture pass cache_len_dev, so no host-to-device copy of the lengths is recorded. */
+#define ZAYA_NOALLOC_SCRATCH_BYTES 67108864
+int zaya_block_decode_noalloc(const zaya_block_config* cfg, const zaya_block_weights* w, int B, const float* x,
+                              const void* router_state_in, float* x_out, void* router_state_out,
+                              const zaya_cca_cache* cache, const zaya_taps* taps, void* stream);
+
 /* Stack: embedding (tied with lm_head), n_layers blocks, final norm, lm_head
  * ("The block": embed_tokens -> layers x 40 -> norm -> lm_head; "The stream is float32
  * whatever the load": the embedding is shifted and scaled, then cast to fp32;

@@ -94,6 +94,9 @@ def lib():
         L.zaya_block_decode.argtypes = [C.POINTER(BlockConfig), C.POINTER(BlockWeights), i, vp, vp, vp, vp,
                                         C.POINTER(CcaCache), C.POINTER(Taps), vp, sz, vp]
         L.zaya_block_decode.restype = i
+        L.zaya_block_decode_noalloc.argtypes = [C.POINTER(BlockConfig), C.POINTER(BlockWeights), i, vp, vp, vp, vp,
+                                                C.POINTER(CcaCache), C.POINTER(Taps), vp]
+        L.zaya_block_decode_noalloc.restype = i
         L.zaya_stack_workspace_bytes.argtypes = [C.POINTER(StackConfig), i, i]
         L.zaya_stack_workspace_bytes.restype = sz
         L.zaya_stack_forward.argtypes = [C.POINTER(StackConfig), C.POINTER(StackWeights), i, i, vp, vp,
@@ -212,6 +215,21 @@ def zaya_block_decode(cfg, w: Mapping, B: int, x, s_in, x_out, s_out, cache, tap
                              _stream(stream))
     del keep
     _check(rc)
+
+
+def zaya_block_decode_noalloc(cfg, w: Mapping, B: int, x, s_in, x_out, s_out, cache, taps=None,
+                              stream=None) -> None:
+    """One decode step in the library's static scratch array, no workspace (see
+    ``zaya_block_decode_noalloc`` in include/zaya.h)."""
+    L = lib()
+    cs, keep = cca_cache(cache)
+    rc = L.zaya_block_decode_noalloc(C.byref(block_config(cfg)), C.byref(block_weights(w)), B, _ptr(x), _ptr(s_in),
+                                     _ptr(x_out), _ptr(s_out), _ref(cs), _ref(taps_struct(taps)), _stream(stream))
+    del keep
+    _check(rc)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ZAYA_NOALLOC_SCRATCH_BYTES
 
 
 def zaya_stack_forward(cfg, sw: Mapping, blocks: Sequence[Mapping], B: int, S: int, ids, logits,

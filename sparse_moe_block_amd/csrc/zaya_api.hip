@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 #include <cstdarg>
 #include <cstdio>
@@ -426,6 +427,37 @@ StackPlan plan_stack(const zaya_stack_config* c, int B, int S) {
   return p;
 }
 
+// ---- allocation-free decode: the workspace is a static device array. Each device the
+// library runs on holds its own copy from the first use until the process ends; its
+// device address comes from hipGetSymbolAddress on that device (the array's name in host
+// code is only a host-side stand-in) and is kept per device.
+constexpr size_t kScratchBytes = ZAYA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up on the first
+// call on that device (with the device current).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZAYA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ZAYA_EHIP, "device %d: only devices 0..%d are served", dev,
+                                                  kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ZAYA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZAYA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +479,23 @@ int zaya_block_decode(const zaya_block_config* cfg, const zaya_block_weights* w,
                       const zaya_taps* taps, void* workspace, size_t workspace_bytes, void* stream) {
   return block_entry(cfg, w, B, 1, true, x, router_state_in, x_out, router_state_out, cache, taps, workspace,
                      workspace_bytes, stream);
+}
+
+int zaya_block_decode_noalloc(const zaya_block_config* cfg, const zaya_block_weights* w, int B, const float* x,
+                              const void* router_state_in, float* x_out, void* router_state_out,
+                              const zaya_cca_cache* cache, const zaya_taps* taps, void* stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (B <= 0) return fail(ZAYA_EINVAL, "B=%d must be positive", B);
+  const size_t need = block_ws_bytes(cfg, B, 1, 1);
+  if (need > kScratchBytes)
+    return fail(ZAYA_EWORKSPACE, "a decode step of %d sequences needs %zu bytes of scratch; the static array holds %zu",
+                B, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return block_entry(cfg, w, B, 1, true, x, router_state_in, x_out, router_state_out, cache, taps, ws, kScratchBytes,
+                     stream);
 }
 
 size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S) {

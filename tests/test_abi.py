@@ -281,3 +281,18 @@ def test_probe_arguments_are_checked(L):
     assert L.zaya_probe_hbm_read(C.c_void_p(FAKE), 4100, 4, C.c_void_p(FAKE), None) == -1  # not 16-byte whole
     assert L.zaya_probe_hbm_read(None, 4096, 4, C.c_void_p(FAKE), None) == -1
 
+
+def test_noalloc_decode_rejects_oversized_steps_before_any_device_call(L):
+    """The allocation-free decode checks the configuration and that the step fits its
+    static array before it looks up the array on a device (nothing here has a GPU)."""
+    cfg = CONFIGS["decode"].replace(batch=128)
+    need = Z.zaya_block_workspace_bytes(cfg, 128, 1, True)
+    assert need > header_define("ZAYA_NOALLOC_SCRATCH_BYTES") == Z.NOALLOC_SCRATCH_BYTES
+    assert Z.zaya_block_workspace_bytes(CONFIGS["decode"], 64, 1, True) <= Z.NOALLOC_SCRATCH_BYTES
+    rc = L.zaya_block_decode_noalloc(C.byref(Z.block_config(cfg)), None, 128, FAKE, FAKE, FAKE, FAKE, None, None,
+                                     None)
+    assert rc == -4 and "static array" in L.zaya_last_error().decode()
+    bad = Z.block_config(cfg.replace(head_dim=80))
+    assert L.zaya_block_decode_noalloc(C.byref(bad), None, 4, FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
+    assert L.zaya_block_decode_noalloc(C.byref(Z.block_config(cfg)), None, 0, FAKE, FAKE, FAKE, FAKE, None, None,
+                                       None) == -1
