@@ -82,13 +82,19 @@ def pack_arena(tensors, dev="cuda"):
 
 
 class Setup:
-    """Device buffers of one block call (no taps)."""
+    """Device buffers of one block call (no taps). bal_bias: balancing biases to use
+    instead of the configuration's (the long-context workload's calibrated ones);
+    weights: device weights to use instead of drawing them (the stack's blocks)."""
 
-    def __init__(self, cfg):
+    def __init__(self, cfg, bal_bias=None, weights=None):
         self.cfg = cfg
         dev = "cuda"
-        w = block_weights(cfg)
-        self.arena, self.w = pack_arena(w, dev)
+        if weights is not None:
+            self.arena, self.w = None, weights
+            w = None
+        else:
+            w = block_weights(cfg, bal_bias=bal_bias)
+            self.arena, self.w = pack_arena(w, dev)
         inp = block_inputs(cfg)
         B, S, H, R = cfg.batch, cfg.seq, cfg.hidden_size, cfg.router_hidden
         self.x = inp["x"].to(dev)
@@ -292,8 +298,8 @@ def time_stages(setup: Setup, steps: int, hip: _Hip):
     return {Z.zaya_stage_name(s): acc[s] / steps for s in range(Z.N_STAGES)}
 
 
-def measure(cfg, steps, warmup, hip):
-    setup = Setup(cfg)
+def measure(cfg, steps, warmup, hip, bal_bias=None, weights=None):
+    setup = Setup(cfg, bal_bias=bal_bias, weights=weights)
     n_routed, n_used, counts = setup.routing()
     ms, wall, ms_med, ms_min = time_steps(setup, steps, warmup, hip)
     graph_ms = time_graph(setup, steps, warmup, hip) if cfg.decode else None
@@ -315,6 +321,54 @@ def measure(cfg, steps, warmup, hip):
     torch.cuda.empty_cache()
     return {"ms": ms, "ms_median": ms_med, "ms_min": ms_min, "graph_ms": graph_ms, "wall": wall, "stages": table, "roofline": roof, "n_routed": n_routed, "experts_used": n_used,
             "expert_counts": counts, "step_gflop": total_f / 1e9, "step_mbytes": total_b / 1e6}
+
+
+def longctx_bias():
+    """The long-context workload's balancing biases (Zipf(1.2) expert load + 15% skip),
+    calibrated by the oracle and stored under tests/golden/."""
+    path = os.path.join(ROOT, "tests", "golden", "longctx_bal_bias.txt")
+    return np.array([float(l) for l in open(path) if l.strip() and not l.startswith("#")], np.float32)
+
+
+def measure_stack(cfg, steps, warmup, hip):
+    """The 40-block stack (embedding, blocks with the router state carried, final norm,
+    tied head) as one zaya_stack_forward call per step, weights drawn on the device
+    (same recipe as the block workloads). Also one block of the stack (block 1, router
+    state fed) timed alone with its stage table, so the head's share follows as the
+    rest: stack - n_layers x block."""
+    from zaya_synth import block_weights_device, stack_weights_device, token_ids
+    B, S, L, V, H = cfg.batch, cfg.seq, cfg.num_layers, cfg.vocab_size, cfg.hidden_size
+    sw = stack_weights_device(cfg)
+    blocks = [block_weights_device(cfg, i) for i in range(L)]
+    ids = token_ids(cfg).to("cuda")
+    logits = torch.empty((B, S, V), device="cuda", dtype=cfg.torch_dtype)
+    ws = torch.empty(Z.zaya_stack_workspace_bytes(cfg, B, S), dtype=torch.uint8, device="cuda")
+
+    class _S:
+        def step(self):
+            Z.zaya_stack_forward(cfg, sw, blocks, B, S, ids, logits, None, None, ws)
+
+    ms, wall, ms_med, ms_min = time_steps(_S(), steps, warmup, hip)
+    del ws
+    torch.cuda.empty_cache()
+    bcfg = cfg.replace(name=cfg.name + "_block", num_layers=1)
+    blk = measure(bcfg, steps, warmup, hip, weights=blocks[1])
+    # work: the blocks' (realized routing of block 1 stands for each block) + the head
+    head_flops = 2.0 * B * S * V * H
+    head_bytes = B * S * H * 2 + V * H * 2 + B * S * V * 2
+    step_gflop = L * blk["step_gflop"] + head_flops / 1e9
+    head_ms = ms - L * blk["ms"]
+    top = max(blk["stages"], key=lambda k: blk["stages"][k]["ms"])
+    if head_ms > L * blk["stages"][top]["ms"]:
+        roof = roofline(head_flops, head_bytes, head_ms)
+        roof["kernel"] = "lm_head (stack time minus the blocks)"
+    else:
+        roof = dict(blk["stages"][top]["roofline"])
+        roof["kernel"] = top + " (per block)"
+    del sw, blocks, logits
+    torch.cuda.empty_cache()
+    return {"ms": ms, "ms_median": ms_med, "ms_min": ms_min, "wall": wall, "step_gflop": step_gflop,
+            "block": blk, "head_ms": head_ms, "roofline": roof}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -365,6 +419,31 @@ def cpu_baseline(cfg):
             "sample": f"{len(runs)} full prefills of the {cfg.seq}-token workload (batch {cfg.batch}) in "
                       f"{sum(runs):.1f} s; median {med:.2f} s, min {min(runs):.2f} s per prefill",
             "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(), "blas": _blas_name()}
+
+
+def cpu_baseline_decode(cfg, budget_s=10.0):
+    """The CPU oracle on the decode workload (64 sequences, one new token each over
+    8192 cached tokens): whole decode steps until about budget_s have passed (at least
+    one); tokens/s from the median step."""
+    from oracle import zaya_oracle as O
+    w = {k: v.float().numpy() for k, v in block_weights(cfg).items()}
+    inp = block_inputs(cfg)
+    x = inp["x"].numpy().astype(np.float64)
+    s = inp["s_in"].float().numpy()
+    cache = {k: inp[k].float().numpy() for k in ("K", "V", "conv_state", "prev_hs")}
+    cache["cache_len"] = inp["cache_len"].numpy()
+    runs = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.block_forward(cfg, w, x, s, cache)
+        runs.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all >= budget_s:
+            break
+    med = float(np.median(runs))
+    return {"value": round(cfg.batch / med, 1), "unit": "tokens/s", "kind": "oracle",
+            "sample": f"{len(runs)} decode steps of the {cfg.batch}-sequence workload over {cfg.kv_len} cached "
+                      f"tokens in {sum(runs):.1f} s; median {med:.2f} s per step"}
 
 
 # ----------------------------------------------------------------------------- ceilings
@@ -465,7 +544,16 @@ def main():
     if not args.no_decode:
         pre2 = measure(CONFIGS["prefill_conv2"], args.steps, args.warmup, hip)
         print(f"[bench] prefill with the two-stage conv {pre2['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    stk = None
+    lc = None
+    if not args.no_decode:
+        lc = measure(CONFIGS["longctx"], max(5, args.steps // 5), max(2, args.warmup // 5), hip,
+                     bal_bias=longctx_bias())
+        print(f"[bench] long-context prefill {lc['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+        stk = measure_stack(CONFIGS["stack"], max(5, args.steps // 5), max(2, args.warmup // 5), hip)
+        print(f"[bench] 40-block stack {stk['ms']:.3f} ms/step", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(pcfg)
+    cpu_dec = None if (args.no_cpu or args.no_decode) else cpu_baseline_decode(CONFIGS["decode"])
     T = pcfg.tokens
     value = T / (pre["ms"] * 1e-3)
     line = {
@@ -505,6 +593,27 @@ def main():
         c2 = CONFIGS["prefill_conv2"]
         line["prefill_two_stage_conv"] = {"tok_s": round(c2.tokens / (pre2["ms"] * 1e-3), 1),
                                           "ms_per_step": round(pre2["ms"], 5), "cca": pre2["stages"]["cca"]}
+    if lc is not None:
+        c4 = CONFIGS["longctx"]
+        line["longctx"] = {
+            "workload": "ZAYA1 block prefill, bf16, batch 1, seq 32768, sliding window 4096, expert load Zipf(1.2) "
+                        "over 16 experts + 15% skip",
+            "tok_s": round(c4.tokens / (lc["ms"] * 1e-3), 1), "ms_per_step": round(lc["ms"], 5),
+            "ms_median": round(lc["ms_median"], 5), "step_gflop": round(lc["step_gflop"], 1),
+            "frac_of_mfma_peak": round(lc["step_gflop"] / (lc["ms"] * 1e-3) / 1e3 / PEAK_BF16_TFLOPS, 4),
+            "routed_tokens": lc["n_routed"], "expert_counts": lc["expert_counts"], "roofline": lc["roofline"],
+            "stages": lc["stages"]}
+    if stk is not None:
+        c3 = CONFIGS["stack"]
+        line["stack"] = {
+            "workload": "40-block ZAYA1 stack + final norm + tied lm_head, bf16, batch 4, seq 2048, vocab 262144",
+            "tok_s": round(c3.tokens / (stk["ms"] * 1e-3), 1), "ms_per_step": round(stk["ms"], 4),
+            "ms_median": round(stk["ms_median"], 4), "step_gflop": round(stk["step_gflop"], 1),
+            "frac_of_mfma_peak": round(stk["step_gflop"] / (stk["ms"] * 1e-3) / 1e3 / PEAK_BF16_TFLOPS, 4),
+            "block_ms": round(stk["block"]["ms"], 5), "head_and_embedding_ms": round(stk["head_ms"], 4),
+            "roofline": stk["roofline"], "block_stages": stk["block"]["stages"]}
+    if cpu_dec is not None and "decode" in line:
+        line["decode"]["cpu_baseline"] = cpu_dec
     if ceil is not None:  # the dominant kernels also against the measured ceilings
         for r in [line["roofline"]] + ([line["decode"]["roofline"]] if "decode" in line else []):
             ref = ceil["hbm_gbs"]["measured"] if r["unit"] == "GB/s" else ceil["mfma_bf16_tflops"]["measured"]

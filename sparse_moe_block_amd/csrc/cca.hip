@@ -102,6 +102,36 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         dst = GC + d / 2 + (cc - segq - segk - segv) * E16;
       }
     };
+    if (a.qkv_part) {
+      // the projection's split-K partials, summed in ascending order from zero and
+      // rounded to T (what the pair's reduction pass would have stored in P)
+      const size_t MN = (size_t)a.B * S * QR;
+      for (int ch = threadIdx.x; ch < nrows * per_row; ch += nthr) {
+        const int rr = ch / per_row, t = t0 - 2 + rr;
+        if (t < 0) continue;
+        int src, dst;
+        chunk_cols(ch % per_row, src, dst);
+        const float* pp = a.qkv_part + ((size_t)b * S + t) * QR + src;
+        float acc[E16];
+#pragma unroll
+        for (int q = 0; q < E16; ++q) acc[q] = 0.f;
+        for (int k0 = 0; k0 < a.kparts; k0 += 8) {  // eight parts' loads at once, summed in order
+          float w[8][E16];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k0 + k < a.kparts)
+#pragma unroll
+              for (int q = 0; q < E16; q += 4) load4(pp + (k0 + k) * MN + q, &w[k][q]);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k0 + k < a.kparts)
+#pragma unroll
+              for (int q = 0; q < E16; ++q) acc[q] += w[k][q];
+        }
+#pragma unroll
+        for (int q = 0; q < E16; q += 4) store4(xs + rr * ROWE + dst + q, acc + q);
+      }
+    } else
     for (int c0 = threadIdx.x; c0 < nrows * per_row; c0 += kBatch * nthr) {
       u32x4 val[kBatch];
 #pragma unroll
@@ -161,9 +191,18 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
           if (i < 2 * GC) xs[(i / GC) * ROWE + i % GC] = hv[k];
         }
       }
-      for (int i = threadIdx.x; i < d / 2; i += nthr)
-        xs[1 * ROWE + GC + d / 2 + i] =
-            fresh ? Act<T>::cvt(0.f) : a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + i];
+      for (int i = threadIdx.x; i < d / 2; i += nthr) {
+        T v = Act<T>::cvt(0.f);
+        if (!fresh && a.vd_part) {
+          const size_t N2 = (size_t)nkv * d / 2, MN2 = (size_t)a.B * N2;
+          float acc = 0.f;
+          for (int kp = 0; kp < a.kparts; ++kp) acc += a.vd_part[kp * MN2 + b * N2 + g * (d / 2) + i];
+          v = Act<T>::cvt(acc);
+        } else if (!fresh) {
+          v = a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + i];
+        }
+        xs[1 * ROWE + GC + d / 2 + i] = v;
+      }
     }
     for (int c0 = threadIdx.x; c0 < GC; c0 += 2 * nthr) {
       float wv[2][4];
@@ -632,6 +671,8 @@ static hipError_t launch_cca_dg(const CcaArgs<T>& a, dim3 grid, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s) {
+  // summed partials: the state write of a chunk longer than one tile reads P itself
+  if (a.qkv_part && (a.S > kCcaTokens || a.conv_k != 3 || !a.vd_part || a.kparts < 1)) return hipErrorInvalidValue;
   dim3 grid((a.S + kCcaTokens - 1) / kCcaTokens, a.nkv, a.B);
   const int G = a.nh / a.nkv;
 #define ZAYA_CCA_CASE(DD, GG) \

@@ -248,6 +248,20 @@ hipError_t launch_gemm_store_pair(const T* A1, int lda1, const T* B1, int ldb1, 
 }
 
 template <typename T>
+int launch_gemm_pair_parts(const T* A1, int lda1, const T* B1, int ldb1, int M1, int N1, const T* A2, int lda2,
+                           const T* B2, int ldb2, int M2, int N2, int K, float* part, size_t part_bytes, hipStream_t s) {
+  constexpr int kBK = 128 / (int)sizeof(T);
+  if (M1 > 64 || M2 > 64 || !part) return 0;
+  const int t1 = ((M1 + 63) / 64) * ((N1 + 63) / 64), t2 = ((M2 + 63) / 64) * ((N2 + 63) / 64);
+  const size_t e1 = (size_t)M1 * N1, e2 = (size_t)M2 * N2;
+  const int kparts = splitk_parts(t1 + t2, K, kBK, e1 + e2, part_bytes);
+  if (kparts == 1) return 0;
+  const SplitProb<T> p1{A1, lda1, B1, ldb1, M1, N1, part}, p2{A2, lda2, B2, ldb2, M2, N2, part + e1 * kparts};
+  hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(t1 + t2, kparts), dim3(256), 0, s, p1, p2, t1, K, kparts);
+  return hipGetLastError() == hipSuccess ? kparts : -1;
+}
+
+template <typename T>
 int launch_gemm_parts(const T* A, int lda, const T* B, int ldb, int M, int N, int K, float* part, size_t part_bytes,
                       hipStream_t s) {
   constexpr int kBK = 128 / (int)sizeof(T);
@@ -282,7 +296,9 @@ hipError_t launch_gemm_router_in(const T* hn, const T* Wd, int M, int R, int H, 
                                                float*, size_t, hipStream_t);                                         \
   template hipError_t launch_gemm_store_pair<T>(const T*, int, const T*, int, int, int, T*, int, const T*, int,      \
                                                 const T*, int, int, int, T*, int, int, float*, size_t, hipStream_t); \
-  template int launch_gemm_parts<T>(const T*, int, const T*, int, int, int, int, float*, size_t, hipStream_t);
+  template int launch_gemm_parts<T>(const T*, int, const T*, int, int, int, int, float*, size_t, hipStream_t);    \
+  template int launch_gemm_pair_parts<T>(const T*, int, const T*, int, int, int, const T*, int, const T*, int, int, \
+                                         int, int, float*, size_t, hipStream_t);
 ZAYA_INST(bf16_t)
 ZAYA_INST(float)
 #undef ZAYA_INST

@@ -32,6 +32,13 @@ hipError_t launch_gemm_store_pair(const T* A1, int lda1, const T* B1, int ldb1, 
 template <typename T>
 int launch_gemm_parts(const T* A, int lda, const T* B, int ldb, int M, int N, int K, float* part, size_t part_bytes,
                       hipStream_t s);
+// Only the split-K partial products of a pair of GEMMs with the same K (as
+// launch_gemm_store_pair): [kparts][M1][N1] at part, then [kparts][M2][N2]; returns
+// kparts (> 1), 0 when not split (nothing launched), -1 on a launch error. The consumer
+// sums the parts in ascending order from zero and rounds, as the pair's reduction would.
+template <typename T>
+int launch_gemm_pair_parts(const T* A1, int lda1, const T* B1, int ldb1, int M1, int N1, const T* A2, int lda2,
+                           const T* B2, int ldb2, int M2, int N2, int K, float* part, size_t part_bytes, hipStream_t s);
 // Sum of the o_proj partials, the attention merge (as the merge epilogue) and the
 // post-attention RMSNorm of the result, one wave per row: writes h (and the
 // attention_output tap) and hn.
@@ -72,6 +79,12 @@ struct CcaArgs {
   int conv_k = 3;         // 3: one depthwise conv; 2: depthwise k2 then grouped k2
   const T* y2 = nullptr;  // conv_k == 2: the convolved q/k channels [B*S][C] (launch_conv2)
   int ring = 0;           // K/V slot of position p: p % cap (else p)
+  // Decode with the kernel-3 conv: P and vdp are not formed; the kernel sums the q/k/v
+  // projection's split-K partials ([kparts][B*S][qkv_ld]) and the delayed value's
+  // ([kparts][B][nkv*d/2]) itself and rounds them (one tile per sequence: S <= 16).
+  const float* qkv_part = nullptr;
+  const float* vd_part = nullptr;
+  int kparts = 0;
 };
 template <typename T>
 hipError_t launch_cca(const CcaArgs<T>& a, hipStream_t s);
@@ -152,6 +165,15 @@ struct RouterArgs {
   T* mlp_tap;      // [T, H] or NULL
   int ntok, R, E, H;
   float eps;
+  // Few tokens: u is not formed by a reduction pass; the kernel sums the router
+  // down-projection's split-K partials ([kparts][ntok][R]) itself, applies its
+  // epilogue (bias, then the carried state times rss when s_in is given) and writes u_out.
+  const float* part = nullptr;
+  int kparts = 0;
+  const T* bd = nullptr;
+  const T* rss = nullptr;
+  const T* s_in = nullptr;
+  T* u_out = nullptr;
 };
 template <typename T>
 hipError_t launch_router(const RouterArgs<T>& a, hipStream_t s);
@@ -179,6 +201,12 @@ struct MoeArgs {
   int ntok, H, I, E;
   const float* gu_scale = nullptr;  // FP8 experts: row scales [E, 2I] and [E, H]
   const float* dn_scale = nullptr;
+  // At most 64 tokens: the gate/up kernel forms the buckets itself from the classes
+  // (each workgroup in LDS) and workgroup 0 stores them to offsets_out / ids_out for
+  // the down kernel and the taps; offsets and ids are then read only by the down kernel.
+  const int32_t* cls = nullptr;
+  int32_t* offsets_out = nullptr;
+  int32_t* ids_out = nullptr;
 };
 template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s);

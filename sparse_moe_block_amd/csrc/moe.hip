@@ -177,6 +177,37 @@ hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, 
   return hipGetLastError();
 }
 
+// Buckets of at most 64 tokens, in the calling workgroup's LDS (wave 0 forms them,
+// then every thread waits): per expert, in expert order, a ballot of the tokens of that
+// class gives the count (the running sum is the offset) and each token's rank among the
+// earlier tokens of its expert gives its slot, so ids stay ascending within an expert.
+// Workgroup 0 also stores them for the kernels that follow. Returns the LDS tables.
+struct SmallBuckets {
+  int off[33];
+  int ids[64];
+};
+__device__ __forceinline__ void small_buckets(const int32_t* __restrict__ cls, int ntok, int E, SmallBuckets& sb,
+                                              int32_t* offsets_out, int32_t* ids_out) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int c = lane < ntok ? cls[lane] : -1;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot(c == e);
+      if (lane == 0) sb.off[e] = run;
+      if (c == e) sb.ids[run + __popcll(m & lt)] = lane;
+      run += __popcll(m);
+    }
+    if (lane == 0) sb.off[E] = run;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if ((int)threadIdx.x <= E) offsets_out[threadIdx.x] = sb.off[threadIdx.x];
+    if ((int)threadIdx.x < sb.off[E]) ids_out[threadIdx.x] = sb.ids[threadIdx.x];
+  }
+}
+
 // ----------------------------------------------------------------------------- grouped GEMMs
 
 // Expert items of 16 rows read each weight tile once: their weight loads may bypass the
@@ -229,12 +260,20 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
   static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  __shared__ SmallBuckets sb;
+  const int32_t* off = a.offsets;
+  const int32_t* ids = a.ids;
+  if (a.cls) {  // few tokens: the buckets are formed here
+    small_buckets(a.cls, a.ntok, a.E, sb, a.offsets_out, a.ids_out);
+    off = sb.off;
+    ids = sb.ids;
+  }
   int e, r0, n_e, j;  // j: activation columns [CN j, CN j + CN)
-  if (!moe_item(a.offsets, a.E, BM, a.I / CN, e, r0, n_e, j)) return;
-  const int base = a.offsets[e] + r0;
+  if (!moe_item(off, a.E, BM, a.I / CN, e, r0, n_e, j)) return;
+  const int base = off[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
-  t.set_a([&](int r) -> const T* { return a.hn + (size_t)a.ids[base + min(r, rows - 1)] * a.H; });
+  t.set_a([&](int r) -> const T* { return a.hn + (size_t)ids[base + min(r, rows - 1)] * a.H; });
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
   t.set_b([&](int r) -> const T* {
     const int blk = r >> 4, w16 = r & 15;
@@ -377,9 +416,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   extern __shared__ __attribute__((aligned(16))) char xs[];  // kF8Tok rows x (K bf16 + 16 bytes)
   const int K = GATEUP ? a.H : a.I;
   const int ntn = (GATEUP ? a.I : a.H) / 64;
+  __shared__ SmallBuckets sb;
+  const int32_t* off = a.offsets;
+  const int32_t* ids = a.ids;
+  if (GATEUP && a.cls) {  // few tokens: the buckets are formed here
+    small_buckets(a.cls, a.ntok, a.E, sb, a.offsets_out, a.ids_out);
+    off = sb.off;
+    ids = sb.ids;
+  }
   int e, r0, n_e, j;
-  if (!moe_item(a.offsets, a.E, kF8Tok, ntn, e, r0, n_e, j)) return;
-  const int base = a.offsets[e] + r0;
+  if (!moe_item(off, a.E, kF8Tok, ntn, e, r0, n_e, j)) return;
+  const int base = off[e] + r0;
   const int rows = min(kF8Tok, n_e - r0);
   const int pitch = K * 2 + 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -415,7 +462,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         if (ch < kF8Tok * cpr) {
           const int r = ch / cpr, cc = ch % cpr;
           const int rr = min(r, rows - 1);
-          const bf16_t* src = GATEUP ? a.hn + (size_t)a.ids[base + rr] * a.H : a.neurons + (size_t)(base + rr) * a.I;
+          const bf16_t* src = GATEUP ? a.hn + (size_t)ids[base + rr] * a.H : a.neurons + (size_t)(base + rr) * a.I;
           v[u] = *reinterpret_cast<const u32x4*>(src + cc * 8);
         }
       }
@@ -497,10 +544,13 @@ static hipError_t launch_f8(const MoeArgs<bf16_t>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
   const int K = GATEUP ? a.H : a.I;
   const size_t lds = (size_t)kF8Tok * (K * 2 + 16);
+  // dynamic LDS up to what the static bucket tables leave of the CU's 160 KiB
+  constexpr int kDyn = 160 * 1024 - 1024;
+  static_assert(sizeof(SmallBuckets) <= 1024, "static LDS of the FP8 expert kernel");
   static const hipError_t attr = hipFuncSetAttribute((const void*)moe_f8_kernel<GATEUP, false>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kDyn);
   static const hipError_t attr_s = hipFuncSetAttribute((const void*)moe_f8_kernel<GATEUP, true>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDyn);
   if (attr != hipSuccess) return attr;
   if (attr_s != hipSuccess) return attr_s;
   const dim3 grid(moe_grid(a.ntok, a.E, kF8Tok, (GATEUP ? a.I : a.H) / 64));

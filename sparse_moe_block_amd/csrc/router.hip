@@ -51,6 +51,45 @@ struct RouterFcFrags {
   }
 };
 
+// bf16: fc1 and fc2 weights pass through LDS, so that the global loads are coalesced
+// (a fragment read straight from memory gives each 16 lanes of a load 16 different
+// rows). The [256 x 256] tile is loaded 16 bytes per thread per step, consecutive
+// threads along a row, and stored with 16-byte chunk c of row r at chunk c ^ (r % 16):
+// both these stores and the fragment reads (16 rows, one chunk) then touch distinct
+// banks. The tile takes 128 KiB of dynamic LDS.
+constexpr int kRouterWBytes = kRouterR * kRouterR * 2;
+constexpr int kRouterStage = kRouterWBytes / 16 / (kRouterWaves * 64);  // 16-byte chunks per thread
+
+struct RouterWStage {
+  u32x4 r[kRouterStage];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ W) {
+#pragma unroll
+    for (int i = 0; i < kRouterStage; ++i)
+      r[i] = *reinterpret_cast<const u32x4*>(W + (size_t)(threadIdx.x + i * kRouterWaves * 64) * 8);
+  }
+  __device__ __forceinline__ void store(char* wl) const {
+#pragma unroll
+    for (int i = 0; i < kRouterStage; ++i) {
+      const int c = threadIdx.x + i * kRouterWaves * 64;
+      const int row = c / 32, lc = c % 32;
+      *reinterpret_cast<u32x4*>(wl + row * 512 + 16 * (lc ^ (row & 15))) = r[i];
+    }
+  }
+};
+
+// The wave's fragments of a weight tile staged in LDS (see RouterWStage).
+__device__ __forceinline__ void router_frags_lds(RouterFcFrags<bf16_t>& W, const char* wl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < kRouterRows / 16; ++nb) {
+    const int row = wave * kRouterRows + nb * 16 + r16;
+#pragma unroll
+    for (int ks = 0; ks < kRouterR / 32; ++ks)
+      W.f[nb][ks].v = *reinterpret_cast<const uint4*>(wl + row * 512 + 16 * ((4 * ks + grp) ^ (row & 15)));
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void router_fc(const RouterFcFrags<T>& W, const T* in_s, T* out_s, int ldsrow) {
   // out[t][n] = rnd(gelu(rnd(sum_k in[t][k] W[n][k] + b[n]))), t < 16, n < 256.
@@ -103,6 +142,13 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
   __shared__ __attribute__((aligned(16))) T a2_s[kRouterTok * ROW];
   __shared__ float lg_s[kRouterTok][33];
   __shared__ int cls_s[kRouterTok];
+  extern __shared__ __attribute__((aligned(16))) char router_wl[];  // bf16: kRouterWBytes
+  constexpr bool kLds = sizeof(T) == 2;
+  RouterWStage st1, st2;
+  if constexpr (kLds) {  // the weight tiles' coalesced loads go out first
+    st1.load(reinterpret_cast<const bf16_t*>(a.W1));
+    st2.load(reinterpret_cast<const bf16_t*>(a.W2));
+  }
 
   const int tok0 = blockIdx.x * kRouterTok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -120,7 +166,40 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
     const int tok = tok0 + wave * 2 + tt;
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[tt][c] = 0.f;
-    if (tok < a.ntok) load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
+    if (tok < a.ntok) {
+      if (a.part) {
+        // u = the down-projection's partials summed in ascending order from zero, then
+        // rnd(+ bias) and, with a carried state, rnd(u + rnd(rss * s_in))
+        // (eight parts' loads issued at once, then summed in order)
+        const size_t MN = (size_t)a.ntok * kRouterR;
+        const float* pp = a.part + (size_t)tok * kRouterR + lane * 4;
+        for (int k0 = 0; k0 < a.kparts; k0 += 8) {
+          float w[8][4];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k0 + k < a.kparts) load4(pp + (k0 + k) * MN, w[k]);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k0 + k < a.kparts)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) v[tt][c] += w[k][c];
+        }
+        float bb[4];
+        load4(a.bd + lane * 4, bb);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[tt][c] = Act<T>::rnd(v[tt][c] + bb[c]);
+        if (a.s_in) {
+          float sc[4], st[4];
+          load4(a.rss + lane * 4, sc);
+          load4(a.s_in + (size_t)tok * kRouterR + lane * 4, st);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[tt][c] = Act<T>::rnd(v[tt][c] + Act<T>::rnd(sc[c] * st[c]));
+        }
+        store4(a.u_out + (size_t)tok * kRouterR + lane * 4, v[tt]);
+      } else {
+        load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
+      }
+    }
   }
   load4(a.norm_g + lane * 4, g);
   RouterFcFrags<T> w1, w2;
@@ -128,8 +207,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
   w2.load_bias(a.b2);
   const float bb1 = r16 < NC ? a.bal_bias[r16] : 0.f;
   const float bb2 = 16 + r16 < NC ? a.bal_bias[16 + r16] : 0.f;
-  w1.load(a.W1);
-  if constexpr (sizeof(T) == 2) w2.load(a.W2);  // fp32 fragments are twice the size: loaded after fc1
+  if constexpr (!kLds) w1.load(a.W1);  // fp32: fragments straight from memory, fc2's after fc1
   typename Mfma<T>::frag wo[kRouterR / 32];
   if (wave < 2) {
     const int c = min(wave * 16 + r16, NC - 1);
@@ -149,12 +227,25 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
     for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(g[c] * Act<T>::rnd(v[tt][c] * inv));
     store4(z_s + (wave * 2 + tt) * ROW + lane * 4, o);
   }
-  __syncthreads();
-  router_fc<T>(w1, z_s, a1_s, ROW);
-  if constexpr (sizeof(T) == 4) w2.load(a.W2);
-  __syncthreads();
-  router_fc<T>(w2, a1_s, a2_s, ROW);
-  __syncthreads();
+  if constexpr (kLds) {
+    st1.store(router_wl);
+    __syncthreads();
+    router_frags_lds(w1, router_wl);
+    router_fc<T>(w1, z_s, a1_s, ROW);
+    __syncthreads();  // every wave has read fc1's tile
+    st2.store(router_wl);
+    __syncthreads();
+    router_frags_lds(w2, router_wl);
+    router_fc<T>(w2, a1_s, a2_s, ROW);
+    __syncthreads();
+  } else {
+    __syncthreads();
+    router_fc<T>(w1, z_s, a1_s, ROW);
+    w2.load(a.W2);
+    __syncthreads();
+    router_fc<T>(w2, a1_s, a2_s, ROW);
+    __syncthreads();
+  }
 
   // out_proj on MFMA: logits[t][c] = rnd(sum_k a2[t][k] Wout[c][k]), waves 0 and 1
   if (wave < 2) {
@@ -209,27 +300,38 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
   }
   __syncthreads();
 
-  // skip tokens: out = (h + rb) * rs + rnd(rnd(hsb) * hss)
-  for (int t = 0; t < kRouterTok; ++t) {
-    const int tok = tok0 + t;
-    if (tok >= a.ntok || cls_s[t] != E) continue;
-    for (int c0 = threadIdx.x * 4; c0 < a.H; c0 += blockDim.x * 4) {
-      float hv[4], b1[4], s1[4], b2[4], s2[4], mo[4], o[4];
-      load4(a.h + (size_t)tok * a.H + c0, hv);
-      load4(a.m_hsb + c0, b1);
-      load4(a.m_hss + c0, s1);
-      load4(a.m_rb + c0, b2);
-      load4(a.m_rs + c0, s2);
+  // skip tokens: out = (h + rb) * rs + rnd(rnd(hsb) * hss). The merge vectors are the
+  // same for every token; the stream rows of all the tile's skip tokens are requested
+  // before any result is stored.
+  unsigned skip = 0;  // bit t: token t of the tile skips
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        mo[c] = Act<T>::rnd(Act<T>::rnd(b1[c]) * s1[c]);
-        o[c] = fadd(fmul(fadd(hv[c], b2[c]), s2[c]), mo[c]);
-      }
-      store4(a.out + (size_t)tok * a.H + c0, o);
-      if (a.mlp_tap) store4(a.mlp_tap + (size_t)tok * a.H + c0, mo);
+  for (int t = 0; t < kRouterTok; ++t)
+    if (tok0 + t < a.ntok && cls_s[t] == E) skip |= 1u << t;
+  if (!skip) return;
+  for (int c0 = threadIdx.x * 4; c0 < a.H; c0 += blockDim.x * 4) {
+    float b1[4], s1[4], b2[4], s2[4], mo[4];
+    float hv[kRouterTok][4];
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t)
+      if ((skip >> t) & 1u) load4(a.h + (size_t)(tok0 + t) * a.H + c0, hv[t]);
+    load4(a.m_hsb + c0, b1);
+    load4(a.m_hss + c0, s1);
+    load4(a.m_rb + c0, b2);
+    load4(a.m_rs + c0, s2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mo[c] = Act<T>::rnd(Act<T>::rnd(b1[c]) * s1[c]);
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) {
+      if (!((skip >> t) & 1u)) continue;
+      const size_t row = (size_t)(tok0 + t) * a.H + c0;
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = fadd(fmul(fadd(hv[t][c], b2[c]), s2[c]), mo[c]);
+      store4(a.out + row, o);
+      if (a.mlp_tap) store4(a.mlp_tap + row, mo);
       if (a.routed_tap) {
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        store4(a.routed_tap + (size_t)tok * a.H + c0, z);
+        store4(a.routed_tap + row, z);
       }
     }
   }
@@ -238,7 +340,14 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
 template <typename T>
 hipError_t launch_router(const RouterArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_kernel<T>, dim3((a.ntok + kRouterTok - 1) / kRouterTok), dim3(kRouterWaves * 64), 0, s,
+  size_t lds = 0;
+  if constexpr (sizeof(T) == 2) {
+    lds = kRouterWBytes;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)router_kernel<T>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRouterWBytes);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL(router_kernel<T>, dim3((a.ntok + kRouterTok - 1) / kRouterTok), dim3(kRouterWaves * 64), lds, s,
                      a);
   return hipGetLastError();
 }

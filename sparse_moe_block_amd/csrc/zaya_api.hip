@@ -231,7 +231,15 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(mark(1));
   float* gpart = p.gpart_bytes ? (float*)(ws + p.gpart) : nullptr;
   const T* Wvd = W(w->W_qkv) + (size_t)(nh * d + nkv * d + nkv * d / 2) * H;
-  if (any_cached && T_ <= 64) {  // few rows: both products share one split-K pass
+  int qkv_kparts = 0;  // > 0: the CCA kernel sums the split-K partials itself
+  if (decode && c->conv_k == 3 && T_ <= 64) {
+    qkv_kparts = launch_gemm_pair_parts<T>(xn, H, W(w->W_qkv), H, T_, QR, prev_hs, H, Wvd, H, B, nkv * d / 2, H,
+                                           gpart, p.gpart_bytes, st);
+    if (qkv_kparts < 0) return fail(ZAYA_EHIP, "q/k/v split-K launch failed");
+  }
+  if (qkv_kparts > 0) {
+    // P and vdp stay as partials
+  } else if (any_cached && T_ <= 64) {  // few rows: both products share one split-K pass
     HIPCHK(launch_gemm_store_pair<T>(xn, H, W(w->W_qkv), H, T_, QR, P, QR, prev_hs, H, Wvd, H, B, nkv * d / 2, vdp,
                                      nkv * d / 2, H, gpart, p.gpart_bytes, st));
   } else {
@@ -251,6 +259,11 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   CcaArgs<T> ca{P, QR, vdp, W(w->conv_w), W(w->conv_b), W(w->temp), conv_state, prev_hs, xn, cl_dev, Q, Kc, Vc, cap,
                 (T*)tp.attention_queries, (T*)tp.attention_keys, (T*)tp.attention_values,
                 B, S, H, nh, nkv, d, c->rope_dim, C, c->rope_theta, c->conv_k, y2, ring};
+  if (qkv_kparts > 0) {
+    ca.qkv_part = gpart;
+    ca.vd_part = gpart + (size_t)T_ * QR * qkv_kparts;
+    ca.kparts = qkv_kparts;
+  }
   HIPCHK(launch_cca<T>(ca, st));
   if (ring_prefill) HIPCHK(launch_ring_store<T>(Kc, Vc, (T*)cache->K, (T*)cache->V, B, nkv, S, d, cache->cap, st));
   // a4: attention
@@ -286,34 +299,58 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(tap_copy(tp.mlp_norm_output, hn, (size_t)T_ * H * A));
   // a7: router down_proj + carried state
   HIPCHK(mark(6));
-  HIPCHK(launch_gemm_router_in<T>(hn, W(w->r_Wd), T_, R, H, W(w->r_bd), W(w->r_rss), (const T*)s_in, (T*)s_out, gpart,
-                                  p.gpart_bytes, st));
+  // few rows: only the split-K partials here; the router kernel sums them
+  const int rparts = T_ <= 64 ? launch_gemm_parts<T>(hn, H, W(w->r_Wd), H, T_, R, H, gpart, p.gpart_bytes, st) : 0;
+  if (rparts < 0) return fail(ZAYA_EHIP, "router split-K launch failed");
+  if (rparts == 0)
+    HIPCHK(launch_gemm_router_in<T>(hn, W(w->r_Wd), T_, R, H, W(w->r_bd), W(w->r_rss), (const T*)s_in, (T*)s_out,
+                                    gpart, p.gpart_bytes, st));
   // a7/a8: router MLP, selection, skip tokens' merge
   HIPCHK(mark(7));
   RouterArgs<T> ra{(const T*)s_out, W(w->r_norm_g), W(w->r_W1), W(w->r_b1), W(w->r_W2), W(w->r_b2), W(w->r_Wout),
                    w->bal_bias, logits, cls, idx, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb), W(w->m_rs), x_out,
                    (T*)tp.routed_output, (T*)tp.mlp_output, T_, R, E, H, c->rms_eps};
+  if (rparts > 0) {
+    ra.part = gpart;
+    ra.kparts = rparts;
+    ra.bd = W(w->r_bd);
+    ra.rss = W(w->r_rss);
+    ra.s_in = (const T*)s_in;
+    ra.u_out = (T*)s_out;
+  }
   HIPCHK(launch_router<T>(ra, st));
   HIPCHK(tap_copy(tp.router_logits, logits, (size_t)T_ * (E + 1) * A));
   HIPCHK(tap_copy(tp.expert_classes, cls, (size_t)T_ * 4));
   HIPCHK(tap_copy(tp.expert_indices, idx, (size_t)T_ * 4));
   HIPCHK(tap_copy(tp.expert_weights, wts, (size_t)T_ * A));
-  // a9: buckets
+  // a9: buckets (at most 64 tokens: formed by the gate/up kernel itself)
   HIPCHK(mark(8));
-  HIPCHK(launch_bucket(cls, T_, E, offsets, ids, st));
-  HIPCHK(tap_copy(tp.bucket_offsets, offsets, (size_t)(E + 1) * 4));
-  HIPCHK(tap_copy(tp.bucket_ids, ids, (size_t)T_ * 4));
+  const bool small_buckets = T_ <= 64;
+  if (!small_buckets) {
+    HIPCHK(launch_bucket(cls, T_, E, offsets, ids, st));
+    HIPCHK(tap_copy(tp.bucket_offsets, offsets, (size_t)(E + 1) * 4));
+    HIPCHK(tap_copy(tp.bucket_ids, ids, (size_t)T_ * 4));
+  }
   // a10/a11: experts, weighted combine, MoE merge
   MoeArgs<T> ma{offsets, ids, hn, W(w->W_gu), W(w->W_dn), neurons, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb),
                 W(w->m_rs), x_out, (T*)tp.routed_output, (T*)tp.mlp_output, T_, H, I, E};
   ma.gu_scale = w->W_gu_scale;
   ma.dn_scale = w->W_dn_scale;
+  if (small_buckets) {
+    ma.cls = cls;
+    ma.offsets_out = offsets;
+    ma.ids_out = ids;
+  }
   const bool f8 = c->expert_format == ZAYA_EXPERTS_FP8_E4M3;  // act is bf16 (checked)
   HIPCHK(mark(9));
   if constexpr (std::is_same<T, bf16_t>::value) {
     HIPCHK(f8 ? launch_moe_gateup_f8(ma, st) : launch_moe_gateup<T>(ma, st));
   } else {
     HIPCHK(launch_moe_gateup<T>(ma, st));
+  }
+  if (small_buckets) {
+    HIPCHK(tap_copy(tp.bucket_offsets, offsets, (size_t)(E + 1) * 4));
+    HIPCHK(tap_copy(tp.bucket_ids, ids, (size_t)T_ * 4));
   }
   HIPCHK(mark(10));
   if constexpr (std::is_same<T, bf16_t>::value) {
