@@ -178,13 +178,24 @@ def stage_work(cfg, n_routed: int, n_used: int):
     return out
 
 
-# Source files each stage's kernels are built from (for matching recorded counters).
+STAGE_NAMES = ["input_norm", "qkv_proj", "cca", "attention", "o_proj_merge", "post_attn_norm", "router_down",
+               "router_mlp_select", "buckets", "expert_gate_up", "expert_down_merge"]
+
+# Source files each stage's kernels are built from (for matching recorded counters);
+# the library's launch sequence (zaya_api.hip) decides which kernels a stage runs.
+_BASE = ["common.h", "kernels.h", "zaya_api.hip"]
 STAGE_SOURCES = {
-    "expert_gate_up": ["moe.hip", "gemm_core.h", "common.h", "kernels.h"],
-    "expert_down_merge": ["moe.hip", "gemm_core.h", "common.h", "kernels.h"],
-    "attention": ["attn.hip", "common.h", "kernels.h"],
-    "qkv_proj": ["gemm.hip", "gemm_core.h", "common.h", "kernels.h"],
-    "o_proj_merge": ["gemm.hip", "gemm_core.h", "common.h", "kernels.h"],
+    "input_norm": ["norm.hip"] + _BASE,
+    "qkv_proj": ["gemm.hip", "gemm_core.h"] + _BASE,
+    "cca": ["cca.hip"] + _BASE,
+    "attention": ["attn.hip"] + _BASE,
+    "o_proj_merge": ["gemm.hip", "gemm_core.h", "norm.hip"] + _BASE,
+    "post_attn_norm": ["norm.hip"] + _BASE,
+    "router_down": ["gemm.hip", "gemm_core.h"] + _BASE,
+    "router_mlp_select": ["router.hip"] + _BASE,
+    "buckets": ["moe.hip"] + _BASE,
+    "expert_gate_up": ["moe.hip", "gemm_core.h"] + _BASE,
+    "expert_down_merge": ["moe.hip", "gemm_core.h"] + _BASE,
 }
 
 
@@ -206,13 +217,19 @@ def recorded_traffic(stage, workload):
         return None
     want = sources_sha256(stage)
     for path in glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md")):
-        rec = {}
+        recs, rec = [], {}
         for line in open(path):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
+                if k.strip() == "stage" and rec:
+                    recs.append(rec)
+                    rec = {}
                 rec[k.strip()] = v.strip().strip("`")
-        if rec.get("stage") == stage and rec.get("workload") == workload and rec.get("sources_sha256") == want:
-            return int(float(rec["hbm_bytes_per_launch"]))
+        if rec:
+            recs.append(rec)
+        for rec in recs:
+            if rec.get("stage") == stage and rec.get("workload") == workload and rec.get("sources_sha256") == want:
+                return int(float(rec["hbm_bytes_per_launch"]))
     return None
 
 
@@ -309,6 +326,8 @@ def measure(cfg, steps, warmup, hip, bal_bias=None, weights=None):
     for name, t in stages.items():
         f, b = work[name]
         r = roofline(f, b, t) if t > 0 and (f or b) else None
+        if r is not None:
+            r["traffic"] = recorded_traffic(name, cfg.name)
         table[name] = {"ms": round(t, 5), "gflop": round(f / 1e9, 3), "mbytes": round(b / 1e6, 3), "roofline": r}
     dom = max(stages, key=lambda k: stages[k])
     f, b = work[dom]
@@ -507,6 +526,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="time only the headline prefill workload")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one workload alone (for counter runs; the JSON line then carries only that one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (a kernel of known traffic for "
                          "scaling hardware byte counters)")
@@ -527,9 +548,18 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     ceil = None if args.copy_calibration else measure_ceilings(hip)
+    if args.only == "decode":
+        dcfg = CONFIGS["decode"]
+        dec = measure(dcfg, args.steps, args.warmup, hip)
+        print(f"[bench] decode {dec['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+        print(json.dumps({"metric": "decode tokens/s (decode workload only)", "value": round(dcfg.batch / (dec["ms"] * 1e-3), 1),
+                          "unit": "tokens/s", "ms_per_step": round(dec["ms"], 5), "stages": dec["stages"]}))
+        return
     pcfg = CONFIGS["prefill"]
     pre = measure(pcfg, args.steps, args.warmup, hip)
     print(f"[bench] prefill {pre['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    if args.only == "prefill":
+        args.no_decode, args.no_cpu = True, True
     dec = None
     if not args.no_decode:
         dcfg = CONFIGS["decode"]
@@ -570,7 +600,8 @@ def main():
         "prefill": {"tok_s": round(value, 1), "ms_median": round(pre["ms_median"], 5), "ms_min": round(pre["ms_min"], 5),
                     "step_gflop": round(pre["step_gflop"], 2),
                     "frac_of_mfma_peak": round(pre["step_gflop"] / (pre["ms"] * 1e-3) / 1e3 / PEAK_BF16_TFLOPS, 4),
-                    "routed_tokens": pre["n_routed"], "experts_used": pre["experts_used"], "stages": pre["stages"],
+                    "routed_tokens": pre["n_routed"], "experts_used": pre["experts_used"],
+                    "expert_counts": pre["expert_counts"], "stages": pre["stages"],
                     "wall_s": round(pre["wall"], 4)},
     }
     if dec is not None:
