@@ -49,7 +49,10 @@ enum zaya_dtype { ZAYA_F32 = 0, ZAYA_BF16 = 1 };
  * one fp32 scale per weight row: the weight is code_value * scale. A low-precision
  * deployment of the experts, like the quantized ZAYA1 bundles (the JANGTQ2 card's
  * "Quantization" section); it needs act_dtype ZAYA_BF16. */
-enum zaya_expert_format { ZAYA_EXPERTS_ACT = 0, ZAYA_EXPERTS_FP8_E4M3 = 1 };
+/* ZAYA_EXPERTS_ACT_PACKED: the act dtype, with W_gu and W_dn in the packed layout that
+ * zaya_pack_experts writes (see there); the arithmetic is that of ZAYA_EXPERTS_ACT, bit for
+ * bit, only the order of the weight bytes in memory differs. */
+enum zaya_expert_format { ZAYA_EXPERTS_ACT = 0, ZAYA_EXPERTS_FP8_E4M3 = 1, ZAYA_EXPERTS_ACT_PACKED = 2 };
 
 enum zaya_status {
   ZAYA_OK = 0,
@@ -285,6 +288,25 @@ size_t zaya_stack_workspace_bytes(const zaya_stack_config* cfg, int B, int S);
 int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w, int B, int S,
                        const int32_t* ids, void* logits, const zaya_cca_cache* caches, const zaya_taps* taps,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Expert weights in the packed layout (weight preparation, done once per block; the
+ * experts are the "Printout"'s ZayaExperts, stacked as the JANGTQ2 card's "Expert layout"
+ * table describes). A grouped expert GEMM streams 128 weight rows at a time, 128 bytes of
+ * K per row per step; row-major, each step touches 128 rows a row length apart. Packed,
+ * the rows come in groups of 128 and each group stores its 128-byte K slices one after
+ * another (slice s of every row of the group, rows in order, then slice s + 1), so a
+ * group is one contiguous run. W_gu [E, 2I, H]: group j of expert e holds 16-row blocks
+ * alternating gate rows 64 j + 16 b .. + 15 and up rows I + 64 j + 16 b .. + 15
+ * (b = 0..3). W_dn [E, H, I]: group g holds rows 128 g .. 128 g + 127.
+ * cfg: the block configuration with act-dtype experts (ZAYA_EXPERTS_ACT or
+ * ZAYA_EXPERTS_ACT_PACKED; ZAYA_EDTYPE for FP8). W_gu, W_dn: row-major device inputs as in
+ * zaya_block_weights. W_gu_packed, W_dn_packed: device outputs of the same byte sizes,
+ * caller-owned, overlapping neither input nor each other (ZAYA_EALIAS). Enqueued on
+ * stream, asynchronous; the inputs may be freed once the stream has passed the copy.
+ * Blocks then run with expert_format ZAYA_EXPERTS_ACT_PACKED and the packed pointers as
+ * W_gu / W_dn. */
+int zaya_pack_experts(const zaya_block_config* cfg, const void* W_gu, const void* W_dn, void* W_gu_packed,
+                      void* W_dn_packed, void* stream);
 
 /* Benchmark instrumentation (not needed for correct use). The block forward runs as
  * ZAYA_N_STAGES stages in this order: input norm, q/k/v projection, CCA projection,

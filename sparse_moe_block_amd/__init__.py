@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzaya.so")
 
 ZAYA_F32, ZAYA_BF16 = 0, 1
-ZAYA_EXPERTS_ACT, ZAYA_EXPERTS_FP8_E4M3 = 0, 1
+ZAYA_EXPERTS_ACT, ZAYA_EXPERTS_FP8_E4M3, ZAYA_EXPERTS_ACT_PACKED = 0, 1, 2
+_EXPERT_FORMATS = {"act": ZAYA_EXPERTS_ACT, "fp8": ZAYA_EXPERTS_FP8_E4M3, "act_packed": ZAYA_EXPERTS_ACT_PACKED}
 STATUS = {0: "ZAYA_OK", -1: "ZAYA_EINVAL", -2: "ZAYA_ESHAPE", -3: "ZAYA_EDTYPE", -4: "ZAYA_EWORKSPACE",
           -5: "ZAYA_ECACHE", -6: "ZAYA_EALIAS", -7: "ZAYA_EHIP"}
 
@@ -102,6 +103,8 @@ def lib():
         L.zaya_stack_forward.argtypes = [C.POINTER(StackConfig), C.POINTER(StackWeights), i, i, vp, vp,
                                          C.POINTER(CcaCache), C.POINTER(Taps), vp, sz, vp]
         L.zaya_stack_forward.restype = i
+        L.zaya_pack_experts.argtypes = [C.POINTER(BlockConfig), vp, vp, vp, vp, vp]
+        L.zaya_pack_experts.restype = i
         L.zaya_last_error.restype = C.c_char_p
         L.zaya_status_str.argtypes = [i]
         L.zaya_status_str.restype = C.c_char_p
@@ -133,7 +136,7 @@ def block_config(cfg) -> BlockConfig:
                        cfg.moe_intermediate_size, cfg.router_hidden, getattr(cfg, "sliding_window", -1),
                        float(getattr(cfg, "rms_norm_eps", 1e-5)),
                        ZAYA_BF16 if cfg.act_dtype == "bf16" else ZAYA_F32,
-                       ZAYA_EXPERTS_FP8_E4M3 if getattr(cfg, "expert_format", "act") == "fp8" else ZAYA_EXPERTS_ACT)
+                       _EXPERT_FORMATS[getattr(cfg, "expert_format", "act")])
 
 
 def block_weights(w: Mapping) -> BlockWeights:
@@ -264,6 +267,23 @@ def zaya_stack_forward(cfg, sw: Mapping, blocks: Sequence[Mapping], B: int, S: i
     _check(rc)
 
 
+def zaya_pack_experts(cfg, W_gu, W_dn, W_gu_packed, W_dn_packed, stream=None) -> None:
+    """Write the packed expert layout (see ``zaya_pack_experts`` in include/zaya.h)."""
+    _check(lib().zaya_pack_experts(C.byref(block_config(cfg)), _ptr(W_gu), _ptr(W_dn), _ptr(W_gu_packed),
+                                   _ptr(W_dn_packed), _stream(stream)))
+
+
+def packed_expert_weights(cfg, w: Mapping, stream=None) -> dict:
+    """A copy of the weight dict whose W_gu / W_dn are new device buffers holding the
+    packed layout of the given row-major ones (for expert_format "act_packed")."""
+    import torch
+    out = dict(w)
+    out["W_gu"] = torch.empty_like(w["W_gu"])
+    out["W_dn"] = torch.empty_like(w["W_dn"])
+    zaya_pack_experts(cfg, w["W_gu"], w["W_dn"], out["W_gu"], out["W_dn"], stream)
+    return out
+
+
 N_STAGES = 11
 
 
@@ -297,7 +317,7 @@ def abi_version() -> int:
     return int(lib().zaya_abi_version())
 
 
-__all__ = ["zaya_block_prefill", "zaya_block_decode", "zaya_stack_forward", "zaya_block_workspace_bytes",
+__all__ = ["zaya_block_prefill", "zaya_block_decode", "zaya_stack_forward", "zaya_pack_experts", "packed_expert_weights", "zaya_block_workspace_bytes",
            "zaya_stack_workspace_bytes", "ZayaError", "ZayaLibraryMissing", "lib", "abi_version", "LIB_PATH",
            "TAP_FIELDS", "WEIGHT_FIELDS", "zaya_set_stage_events", "zaya_stage_name", "N_STAGES",
            "zaya_probe_mfma_bf16", "zaya_probe_hbm_read"]

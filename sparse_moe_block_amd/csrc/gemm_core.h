@@ -46,6 +46,9 @@ struct GemmTile {
   f32x4 acc[kTM][kTN];
   const char* pa[kAChunks];
   const char* pb[kBChunks];
+  // Bytes from one K slice of a B row to the next: one slice (kRowBytes) for row-major
+  // operands; a packed operand stores the slices of a row group one after another.
+  size_t bstride = kRowBytes;
 
   // LDS rows are 128 bytes (eight 16-byte chunks) with no padding; chunk j of row r is
   // stored at position j ^ swz(r), swz(r) = (r / 2) % 8. A fragment read has lanes
@@ -89,13 +92,13 @@ struct GemmTile {
   }
 
   __device__ __forceinline__ void load_slice(int kt, u32x4* ra, u32x4* rb) const {
-    const size_t off = (size_t)kt * kRowBytes;
+    const size_t off = (size_t)kt * kRowBytes, boff = (size_t)kt * bstride;
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + off);
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
-      if constexpr (STREAM_B) rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pb[i] + off));
-      else rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + off);
+      if constexpr (STREAM_B) rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pb[i] + boff));
+      else rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + boff);
     }
   }
 

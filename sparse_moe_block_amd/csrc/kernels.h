@@ -207,7 +207,16 @@ struct MoeArgs {
   const int32_t* cls = nullptr;
   int32_t* offsets_out = nullptr;
   int32_t* ids_out = nullptr;
+  // W_gu / W_dn in the packed layout of launch_pack_experts (act-dtype experts only)
+  int packed = 0;
 };
+// Packed expert weights: rows in groups of kPackRows, each group stored slice after
+// slice (kPackSliceBytes of every row of the group, row after row), groups of an
+// expert after one another. W_gu groups hold the gate/up items' row order (see moe.hip).
+constexpr int kPackRows = 128;
+constexpr int kPackSliceBytes = 128;
+template <typename T>
+hipError_t launch_pack_experts(const T* Wgu, const T* Wdn, T* Pgu, T* Pdn, int E, int H, int I, hipStream_t s);
 template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s);
 // FP8 (E4M3) expert weights with fp32 row scales, bf16 activations

@@ -208,6 +208,59 @@ __device__ __forceinline__ void small_buckets(const int32_t* __restrict__ cls, i
   }
 }
 
+// ----------------------------------------------------------------------------- packed expert weights
+//
+// A grouped-GEMM item streams the K slices (128 bytes of a row) of 128 weight rows. In
+// the row-major layout those 128 x 128 bytes lie 128 row lengths apart, so each slice
+// load opens as many DRAM pages; packed, the slices of a 128-row group follow one
+// another (group-major, then slice, then row), so an item reads one contiguous run of
+// HBM. Group j of W_gu holds the rows a gate/up item uses, in its order: 16-row blocks
+// alternating gate (rows 64 j + 16 b ..) and up (rows I + 64 j + 16 b ..). Group g of
+// W_dn holds rows 128 g .. 128 g + 127. Both are plain permutations of 16-byte chunks.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void pack_experts_kernel(const char* __restrict__ src, char* __restrict__ dst,
+                                                           size_t nchunks, int rows_e, int row_bytes, int I) {
+  const int ns = row_bytes / kPackSliceBytes;  // slices per row
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nchunks; i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i & 7);
+    const int q = (int)((i >> 3) % kPackRows);
+    const size_t gs = i / (8 * kPackRows);  // (expert, group, slice)
+    const int s = (int)(gs % ns);
+    const size_t eg = gs / ns;
+    const int ng = rows_e / kPackRows;
+    const int grp = (int)(eg % ng), e = (int)(eg / ng);
+    int row;
+    if constexpr (GATEUP) {
+      const int blk = q >> 4;
+      row = ((blk & 1) ? I : 0) + 64 * grp + (blk >> 1) * 16 + (q & 15);
+    } else {
+      row = grp * kPackRows + q;
+    }
+    const size_t from = ((size_t)e * rows_e + row) * row_bytes + (size_t)s * kPackSliceBytes + c * 16;
+    *reinterpret_cast<u32x4*>(dst + i * 16) = *reinterpret_cast<const u32x4*>(src + from);
+  }
+}
+
+template <typename T>
+hipError_t launch_pack_experts(const T* Wgu, const T* Wdn, T* Pgu, T* Pdn, int E, int H, int I, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  if ((2 * I) % kPackRows || H % kPackRows || (H * (int)sizeof(T)) % kPackSliceBytes ||
+      (I * (int)sizeof(T)) % kPackSliceBytes)
+    return hipErrorInvalidValue;
+  const size_t ngu = (size_t)E * 2 * I * H * sizeof(T) / 16, ndn = (size_t)E * H * I * sizeof(T) / 16;
+  const int grid = 256 * 8;
+  hipLaunchKernelGGL(pack_experts_kernel<true>, dim3(grid), dim3(256), 0, s, reinterpret_cast<const char*>(Wgu),
+                     reinterpret_cast<char*>(Pgu), ngu, 2 * I, H * (int)sizeof(T), I);
+  hipLaunchKernelGGL(pack_experts_kernel<false>, dim3(grid), dim3(256), 0, s, reinterpret_cast<const char*>(Wdn),
+                     reinterpret_cast<char*>(Pdn), ndn, H, I * (int)sizeof(T), I);
+  return hipGetLastError();
+}
+
+template hipError_t launch_pack_experts<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, bf16_t*, int, int, int,
+                                                 hipStream_t);
+template hipError_t launch_pack_experts<float>(const float*, const float*, float*, float*, int, int, int,
+                                                hipStream_t);
+
 // ----------------------------------------------------------------------------- grouped GEMMs
 
 // Expert items of 16 rows read each weight tile once: their weight loads may bypass the
@@ -259,6 +312,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   constexpr int CN = BN / 2;  // activation columns per item
   using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
   static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
+  static_assert(Tile::kRowBytes == kPackSliceBytes, "packed slices are the tile's K slices");
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
   __shared__ SmallBuckets sb;
   const int32_t* off = a.offsets;
@@ -275,11 +329,18 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   Tile t;
   t.set_a([&](int r) -> const T* { return a.hn + (size_t)ids[base + min(r, rows - 1)] * a.H; });
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
-  t.set_b([&](int r) -> const T* {
-    const int blk = r >> 4, w16 = r & 15;
-    const int row = ((blk & 1) ? a.I : 0) + CN * j + (blk >> 1) * 16 + w16;
-    return Wg + (size_t)row * a.H;
-  });
+  if (a.packed) {  // the item's 128 rows are packed group j, in the same row order
+    static_assert(BN == kPackRows, "a gate/up item is one packed row group");
+    const T* Wgrp = Wg + (size_t)j * kPackRows * a.H;
+    t.set_b([&](int r) -> const T* { return Wgrp + (size_t)r * Tile::kBK; });
+    t.bstride = (size_t)kPackRows * Tile::kRowBytes;
+  } else {
+    t.set_b([&](int r) -> const T* {
+      const int blk = r >> 4, w16 = r & 15;
+      const int row = ((blk & 1) ? a.I : 0) + CN * j + (blk >> 1) * 16 + w16;
+      return Wg + (size_t)row * a.H;
+    });
+  }
   t.run(smem, a.H / Tile::kBK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -318,7 +379,15 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   Tile t;
   t.set_a([&](int r) -> const T* { return a.neurons + (size_t)(base + min(r, rows - 1)) * a.I; });
   const T* Wd = a.W_dn + (size_t)e * a.H * a.I;
-  t.set_b([&](int r) -> const T* { return Wd + (size_t)(n0 + r) * a.I; });
+  if (a.packed) {  // rows n0 .. n0 + BN lie in packed group n0 / 128
+    static_assert(kPackRows % BN == 0, "a down item lies in one packed row group");
+    const T* Wgrp = Wd + (size_t)(n0 / kPackRows) * kPackRows * a.I;
+    const int q0 = n0 % kPackRows;
+    t.set_b([&](int r) -> const T* { return Wgrp + (size_t)(q0 + r) * Tile::kBK; });
+    t.bstride = (size_t)kPackRows * Tile::kRowBytes;
+  } else {
+    t.set_b([&](int r) -> const T* { return Wd + (size_t)(n0 + r) * a.I; });
+  }
   t.run(smem, a.I / Tile::kBK);
   t.epilogue([&](int m, int nl, const float* v) {
     if (m >= rows) return;

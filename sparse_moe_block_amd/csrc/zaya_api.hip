@@ -62,7 +62,8 @@ int check_config(const zaya_block_config* c) {
   if (c->router_hidden != 256) return fail(ZAYA_ESHAPE, "router_hidden %d != 256", c->router_hidden);
   if (!(c->rms_eps > 0.f)) return fail(ZAYA_ESHAPE, "rms_eps must be > 0");
   if (!(c->rope_theta > 0.f)) return fail(ZAYA_ESHAPE, "rope_theta must be > 0");
-  if (c->expert_format != ZAYA_EXPERTS_ACT && c->expert_format != ZAYA_EXPERTS_FP8_E4M3)
+  if (c->expert_format != ZAYA_EXPERTS_ACT && c->expert_format != ZAYA_EXPERTS_FP8_E4M3 &&
+      c->expert_format != ZAYA_EXPERTS_ACT_PACKED)
     return fail(ZAYA_EDTYPE, "expert_format %d", c->expert_format);
   if (c->expert_format == ZAYA_EXPERTS_FP8_E4M3) {
     if (c->act_dtype != ZAYA_BF16) return fail(ZAYA_EDTYPE, "FP8 experts need act_dtype ZAYA_BF16");
@@ -336,6 +337,7 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
                 W(w->m_rs), x_out, (T*)tp.routed_output, (T*)tp.mlp_output, T_, H, I, E};
   ma.gu_scale = w->W_gu_scale;
   ma.dn_scale = w->W_dn_scale;
+  ma.packed = c->expert_format == ZAYA_EXPERTS_ACT_PACKED;
   if (small_buckets) {
     ma.cls = cls;
     ma.offsets_out = offsets;
@@ -608,6 +610,32 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
                                    (float*)logits, cfg->vocab, nullptr, 0, st);
   }
   if (e != hipSuccess) return fail(ZAYA_EHIP, "final norm / lm_head: %s", hipGetErrorString(e));
+  return ZAYA_OK;
+}
+
+int zaya_pack_experts(const zaya_block_config* cfg, const void* W_gu, const void* W_dn, void* W_gu_packed,
+                      void* W_dn_packed, void* stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (cfg->expert_format == ZAYA_EXPERTS_FP8_E4M3)
+    return fail(ZAYA_EDTYPE, "zaya_pack_experts packs act-dtype experts, not FP8 codes");
+  if (!W_gu || !W_dn || !W_gu_packed || !W_dn_packed) return fail(ZAYA_EINVAL, "expert weight pointer is NULL");
+  const int E = cfg->n_experts, H = cfg->hidden, I = cfg->expert_inter;
+  const size_t A = act_bytes(cfg);
+  const size_t ngu = (size_t)E * 2 * I * H * A, ndn = (size_t)E * H * I * A;
+  if (overlap(W_gu_packed, ngu, W_gu, ngu) || overlap(W_gu_packed, ngu, W_dn, ndn) ||
+      overlap(W_dn_packed, ndn, W_gu, ngu) || overlap(W_dn_packed, ndn, W_dn, ndn) ||
+      overlap(W_gu_packed, ngu, W_dn_packed, ndn))
+    return fail(ZAYA_EALIAS, "packed expert weights overlap the row-major ones or each other");
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e =
+      cfg->act_dtype == ZAYA_BF16
+          ? launch_pack_experts<bf16_t>((const bf16_t*)W_gu, (const bf16_t*)W_dn, (bf16_t*)W_gu_packed,
+                                        (bf16_t*)W_dn_packed, E, H, I, st)
+          : launch_pack_experts<float>((const float*)W_gu, (const float*)W_dn, (float*)W_gu_packed,
+                                       (float*)W_dn_packed, E, H, I, st);
+  if (e != hipSuccess) return fail(ZAYA_EHIP, "expert packing: %s", hipGetErrorString(e));
   return ZAYA_OK;
 }
 

@@ -296,3 +296,21 @@ def test_noalloc_decode_rejects_oversized_steps_before_any_device_call(L):
     assert L.zaya_block_decode_noalloc(C.byref(bad), None, 4, FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
     assert L.zaya_block_decode_noalloc(C.byref(Z.block_config(cfg)), None, 0, FAKE, FAKE, FAKE, FAKE, None, None,
                                        None) == -1
+
+
+def test_pack_experts_validation(L):
+    """zaya_pack_experts: act-dtype experts only, no NULL pointer, packed buffers that
+    overlap neither the row-major ones nor each other. Every case fails before a launch."""
+    cfg = CONFIGS["prefill"]
+    E, H, I = cfg.num_experts, cfg.hidden_size, cfg.moe_intermediate_size
+    ngu, ndn = E * 2 * I * H * 2, E * H * I * 2
+    gu, dn = FAKE, FAKE + ngu  # two dummy row-major buffers, back to back
+    pgu, pdn = FAKE + ngu + ndn, FAKE + 2 * ngu + ndn
+    pack = lambda c, *p: L.zaya_pack_experts(C.byref(Z.block_config(c)), *[C.c_void_p(v) if v else None for v in p],
+                                             None)
+    assert pack(CONFIGS["decode_fp8"], gu, dn, pgu, pdn) == -3
+    assert "FP8" in L.zaya_last_error().decode()
+    assert pack(cfg, gu, dn, None, pdn) == -1
+    assert pack(cfg, gu, dn, dn + 4096, pdn) == -6  # packed W_gu over the row-major W_dn
+    assert pack(cfg, gu, dn, pgu, pgu + ngu - 2) == -6  # the two packed buffers overlap
+    assert pack(cfg.replace(hidden_size=2000), gu, dn, pgu, pdn) == -2

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import sparse_moe_block_amd as Z
-from tests.zaya_harness import DEV
+from tests.zaya_harness import DEV, pack_if_needed
 from zaya_synth import CONFIGS, _device_stream, block_weights_device
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def _caches(cfg, n_blocks):
 def test_graph_captured_decode_step_is_bit_identical_to_eager():
     cfg = CONFIGS["decode"]
     B, H, R = cfg.batch, cfg.hidden_size, cfg.router_hidden
-    blocks = [block_weights_device(cfg, l) for l in range(L_BLOCKS)]
+    blocks = [pack_if_needed(cfg, block_weights_device(cfg, l)) for l in range(L_BLOCKS)]
     caches = _caches(cfg, L_BLOCKS)
     pos = cfg.kv_len
     g0 = _device_stream(0, cfg.name + "_graph", -1, "x", DEV)
@@ -119,7 +119,7 @@ def test_graph_replay_with_grown_cache_length_matches_oracle():
     B, H, R, E = cfg.batch, cfg.hidden_size, cfg.router_hidden, cfg.num_experts
     w_host = block_weights(cfg)
     inp = block_inputs(cfg)  # K/V filled to 1100 positions, cap 1101
-    w = upload_weights(w_host)
+    w = upload_weights(w_host, cfg)
     cache = {k: inp[k].to(DEV).contiguous() for k in ("K", "V", "conv_state", "prev_hs")}
     cache["cache_len"] = [L_cap] * B
     cache["cache_len_dev"] = torch.full((B,), L_cap, dtype=torch.int32, device=DEV)

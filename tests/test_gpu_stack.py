@@ -6,7 +6,7 @@ import torch
 
 import sparse_moe_block_amd as Z
 from oracle import zaya_oracle as O
-from tests.zaya_harness import DEV, TOL, compare, stream_bound, to_np
+from tests.zaya_harness import DEV, TOL, compare, pack_if_needed, stream_bound, to_np
 from zaya_synth import (CONFIGS, block_weights, block_weights_device, stack_weights, stack_weights_device,
                         token_ids)
 
@@ -91,7 +91,9 @@ def test_full_stack_workload_blockwise():
     ids_h = token_ids(cfg)
     taps = [_taps(cfg) for _ in range(L)]
     t0 = time.time()
-    logits = _run_stack(cfg, sw, blocks, ids_h.to(DEV), taps)
+    # the library reads the packed expert layout; the oracle below reads the row-major one
+    logits = _run_stack(cfg, sw, [pack_if_needed(cfg, b) for b in blocks], ids_h.to(DEV), taps)
+    torch.cuda.empty_cache()
     seqs = [0, B - 1]
     bcfg = cfg.replace(batch=len(seqs), seq=S)
     rng = np.random.default_rng(7)

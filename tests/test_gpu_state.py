@@ -132,7 +132,7 @@ def test_prefill_then_decode_equals_oracle_prefill(conv_k, ring):
                                      sliding_window=W, **_conv_kw(conv_k))
     w_host = block_weights(cfg)
     inp = block_inputs(cfg)  # x [B, S+1, H], s_in [B, S+1, R]
-    w = upload_weights(w_host)
+    w = upload_weights(w_host, cfg)
     H, R, nkv, d, C = cfg.hidden_size, cfg.router_hidden, cfg.num_kv_heads, cfg.head_dim, cfg.conv_channels
     dt = cfg.torch_dtype
     cap = W + 1 if ring else S + 1

@@ -33,7 +33,7 @@ def _taps(cfg):
 
 def _one(cfg, lens):
     B, H, R = cfg.batch, cfg.hidden_size, cfg.router_hidden
-    w = upload_weights(block_weights(cfg))
+    w = upload_weights(block_weights(cfg), cfg)
     inp = block_inputs(cfg)
     base = {k: inp[k].to(DEV).contiguous() for k in ("K", "V", "conv_state", "prev_hs")}
     x, s_in = inp["x"].to(DEV), inp["s_in"].to(DEV)

@@ -207,8 +207,18 @@ def cca_bound(cfg, w, xn_gpu, xn_ref, cache_len, conv_state, prev_hs, act: str):
     return cca["Q"], cca["K"], bq, bk
 
 
-def upload_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
-    return {k: v.to(DEV).contiguous() for k, v in w.items()}
+def pack_if_needed(cfg, w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+    """Device weights in the expert layout the configuration names: with expert_format
+    "act_packed" the library's zaya_pack_experts lays out the row-major W_gu / W_dn."""
+    if getattr(cfg, "expert_format", "act") != "act_packed":
+        return w
+    out = Z.packed_expert_weights(cfg, w)
+    torch.cuda.synchronize()
+    return out
+
+
+def upload_weights(w: Dict[str, torch.Tensor], cfg) -> Dict[str, torch.Tensor]:
+    return pack_if_needed(cfg, {k: v.to(DEV).contiguous() for k, v in w.items()})
 
 
 def np_weights(w: Dict[str, torch.Tensor]) -> Dict[str, np.ndarray]:
@@ -225,7 +235,7 @@ class BlockRun:
         self.w_host = block_weights(cfg, seed=seed) if w_host is None else w_host
         self.inp = block_inputs(cfg, seed=seed) if inp is None else inp
         self.decode = cfg.decode if decode is None else decode
-        self.w = upload_weights(self.w_host)
+        self.w = upload_weights(self.w_host, cfg)
         B, S, H, R = cfg.batch, cfg.seq, cfg.hidden_size, cfg.router_hidden
         nh, nkv, d, E, I = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.num_experts, cfg.moe_intermediate_size
         T = B * S
