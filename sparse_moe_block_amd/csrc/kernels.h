@@ -174,12 +174,20 @@ struct RouterArgs {
   const T* rss = nullptr;
   const T* s_in = nullptr;
   T* u_out = nullptr;
+  // tokens of each class c in workgroup r's tile at counts[c * counts_ld + r] (for the
+  // buckets), or NULL
+  int32_t* counts = nullptr;
+  int counts_ld = 0;
 };
+constexpr int kRouterTokens = 16;  // tokens per router workgroup
 template <typename T>
 hipError_t launch_router(const RouterArgs<T>& a, hipStream_t s);
 
 // ---- mixture of experts
-hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, int32_t* ids, hipStream_t s);
+// counts: the router's per-tile class counts, class c of tile r at c * bucket_counts_ld(ntok) + r
+int bucket_counts_ld(int ntok);
+hipError_t launch_bucket(const int32_t* cls, const int32_t* counts, int ntok, int E, int32_t* offsets, int32_t* ids,
+                         hipStream_t s);
 
 template <typename T>
 struct MoeArgs {

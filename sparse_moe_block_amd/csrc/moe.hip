@@ -26,154 +26,106 @@ namespace zaya {
 
 // ----------------------------------------------------------------------------- buckets
 
-// One workgroup of 1024 threads. Tokens are taken in passes of up to kBucketPer
-// chunks of 1024 (chunk j: tokens pass0 + 1024 j + tid) whose classes are loaded at
-// once and kept in registers (up to 8192 tokens the second sweep reuses them). Counts
-// use LDS atomics; placement ranks each token among the same-expert tokens of its wave
-// with ballots and adds the counts of the earlier waves, chunk by chunk, so ids stay
-// ascending within an expert.
-constexpr int kBucketPer = 8;
+// One workgroup per kBucketTok tokens, all independent. The router leaves per-class
+// token counts of each of its 16-token tiles (counts[c * ld + r], ld a multiple of 4).
+// Thread (class c, segment g) sums row c over its segment of the tiles with 16-byte
+// loads issued eight at a time (indices clamped, sums masked, so nothing waits inside a
+// batch), separately for the tiles before this workgroup's chunk and for all tiles; the
+// segments are then added in LDS. That gives every expert's offset (an exclusive scan
+// over the experts' totals) and its tokens in earlier chunks. The chunk's tokens are
+// placed by their ballot rank within the wave plus the counts of the earlier waves, so
+// ids stay ascending within an expert. Skip tokens (class E) get no slot.
+constexpr int kBucketTok = 1024;
 
-__global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict__ cls, int ntok, int E,
-                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ ids) {
-  __shared__ int cnt[32];
-  __shared__ int base[32];
-  __shared__ int wcnt[16][32];
+template <int CB>  // classes the thread grid covers (E <= CB)
+__global__ __launch_bounds__(kBucketTok) void bucket_kernel(const int32_t* __restrict__ cls,
+                                                            const int32_t* __restrict__ counts, int ld, int ntok,
+                                                            int E, int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ ids) {
+  constexpr int NW = kBucketTok / 64, SEG = kBucketTok / CB;
+  __shared__ int part[2][CB][SEG + 1];  // per (class, segment): counts before the chunk, totals
+  __shared__ int base[32];              // expert offset + its tokens in earlier chunks
+  __shared__ int wcnt[NW][32];          // the chunk's tokens per expert, per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrw = (ntok + kRouterTokens - 1) / kRouterTokens;
+  const int r_end = blockIdx.x * (kBucketTok / kRouterTokens);  // router tiles before this chunk
+  const int t = blockIdx.x * kBucketTok + tid;
+  const int k = t < ntok ? cls[t] : -1;
+  {
+    const int c = tid / SEG, g = tid % SEG;
+    const int nq = ld / 4;                  // 16-byte chunks per row
+    const int per = (nq + SEG - 1) / SEG;   // chunks per segment
+    const int q0 = g * per, q1 = min(q0 + per, nq);
+    const int4* row = reinterpret_cast<const int4*>(counts + (size_t)min(c, E - 1) * ld);
+    int bef = 0, tot = 0;
+    for (int qb = q0; qb < q1; qb += 8) {
+      int4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = row[min(qb + j, nq - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 4 * (qb + j);
+        const int x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool in = qb + j < q1 && r + i < nrw;
+          tot += in ? x[i] : 0;
+          bef += in && r + i < r_end ? x[i] : 0;
+        }
+      }
+    }
+    part[0][c][g] = bef;
+    part[1][c][g] = tot;
+  }
+  // ranks of this wave's tokens among the same expert's
   const unsigned long long lt = (1ull << lane) - 1ull;
-  const bool single = ntok <= kBucketPer * 1024;
-  int c[kBucketPer];
-  auto load = [&](int pass0) {
-#pragma unroll
-    for (int j = 0; j < kBucketPer; ++j) {
-      const int t = pass0 + j * 1024 + tid;
-      c[j] = t < ntok ? cls[t] : -1;
-    }
-  };
-  if (tid < 32) cnt[tid] = 0;
+  int rank = 0, mine = 0;
+  for (int e = 0; e < E; ++e) {
+    const unsigned long long m = __ballot(k == e);
+    if (lane == e) mine = __popcll(m);
+    if (k == e) rank = __popcll(m & lt);
+  }
+  if (lane < E) wcnt[wave][lane] = mine;
   __syncthreads();
-  for (int pass0 = 0; pass0 < ntok; pass0 += kBucketPer * 1024) {
-    load(pass0);
+  if (wave == 0) {
+    int bef = 0, tot = 0;
+    if (lane < E)
+      for (int g = 0; g < SEG; ++g) {
+        bef += part[0][lane][g];
+        tot += part[1][lane][g];
+      }
+    int incl = tot;
 #pragma unroll
-    for (int j = 0; j < kBucketPer; ++j)
-      if (c[j] >= 0 && c[j] < E) atomicAdd(&cnt[c[j]], 1);
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane < E) base[lane] = incl - tot + bef;
+    if (blockIdx.x == 0) {
+      if (lane < E) offsets[lane] = incl - tot;
+      if (lane == E - 1) offsets[E] = incl;
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = run;
-      offsets[e] = run;
-      run += cnt[e];
-    }
-    offsets[E] = run;
-  }
-  __syncthreads();
-  for (int pass0 = 0; pass0 < ntok; pass0 += kBucketPer * 1024) {
-    if (!single) load(pass0);
-    const int nch = min(kBucketPer, (ntok - pass0 + 1023) / 1024);
-#pragma unroll
-    for (int j = 0; j < kBucketPer; ++j) {
-      if (j >= nch) break;
-      int rank = 0;
-      for (int e = 0; e < E; ++e) {
-        const unsigned long long m = __ballot(c[j] == e);
-        if (lane == 0) wcnt[wave][e] = __popcll(m);
-        if (c[j] == e) rank = __popcll(m & lt);
-      }
-      __syncthreads();
-      if (c[j] >= 0 && c[j] < E) {
-        int pos = base[c[j]] + rank;
-        for (int w = 0; w < wave; ++w) pos += wcnt[w][c[j]];
-        ids[pos] = pass0 + j * 1024 + tid;
-      }
-      __syncthreads();
-      if (tid < E) {
-        int add = 0;
-        for (int w = 0; w < 16; ++w) add += wcnt[w][tid];
-        base[tid] += add;
-      }
-      __syncthreads();
-    }
+  if (k >= 0 && k < E) {
+    int pos = base[k] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][k];
+    ids[pos] = t;
   }
 }
 
-// Up to kBucketPer * 1024 tokens in one sweep: every thread keeps its classes in
-// registers; per (chunk, wave, expert) counts come from ballots, one wave per expert
-// scans them into that expert's running prefix in (chunk, wave) order, and each token's
-// slot is its expert's offset + the prefix of its (chunk, wave) + its rank in the wave.
-// Three barriers in all.
-__global__ __launch_bounds__(1024) void bucket_small_kernel(const int32_t* __restrict__ cls, int ntok, int E,
-                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ ids) {
-  __shared__ int wpre[kBucketPer][16][32];  // counts, then exclusive prefixes within an expert
-  __shared__ int base[32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  const int nch = (ntok + 1023) / 1024;
-  int c[kBucketPer], rank[kBucketPer];
-#pragma unroll
-  for (int j = 0; j < kBucketPer; ++j) {
-    const int t = j * 1024 + tid;
-    c[j] = t < ntok ? cls[max(min(t, ntok - 1), 0)] : -1;
-  }
-#pragma unroll
-  for (int j = 0; j < kBucketPer; ++j) {
-    if (j >= nch) break;
-    int mine = 0;
-    rank[j] = 0;
-    for (int e = 0; e < E; ++e) {
-      const unsigned long long m = __ballot(c[j] == e);
-      if (lane == e) mine = __popcll(m);
-      if (c[j] == e) rank[j] = __popcll(m & lt);
-    }
-    if (lane < E) wpre[j][wave][lane] = mine;
-  }
-  __syncthreads();
-  // wave w scans the (chunk, wave) counts of experts w, w + 16 (two entries per lane)
-  for (int e = wave; e < E; e += 16) {
-    const int n = nch * 16, k0 = 2 * lane;
-    const int v0 = k0 < n ? wpre[k0 >> 4][k0 & 15][e] : 0;
-    const int v1 = k0 + 1 < n ? wpre[(k0 + 1) >> 4][(k0 + 1) & 15][e] : 0;
-    int incl = v0 + v1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    const int excl = incl - v0 - v1;
-    if (k0 < n) wpre[k0 >> 4][k0 & 15][e] = excl;
-    if (k0 + 1 < n) wpre[(k0 + 1) >> 4][(k0 + 1) & 15][e] = excl + v0;
-    const int total = __shfl(incl, 63, 64);
-    if (lane == 0) base[e] = total;
-  }
-  __syncthreads();
-  if (wave == 0) {  // expert offsets: exclusive scan of the counts
-    const int n = lane < E ? base[lane] : 0;
-    int incl = n;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    if (lane < E) {
-      base[lane] = incl - n;
-      offsets[lane] = incl - n;
-    }
-    if (lane == E - 1) offsets[E] = incl;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kBucketPer; ++j) {
-    if (j >= nch) break;
-    if (c[j] >= 0 && c[j] < E) ids[base[c[j]] + wpre[j][wave][c[j]] + rank[j]] = j * 1024 + tid;
-  }
-}
+int bucket_counts_ld(int ntok) { return ((ntok + kRouterTokens - 1) / kRouterTokens + 3) / 4 * 4; }
 
-hipError_t launch_bucket(const int32_t* cls, int ntok, int E, int32_t* offsets, int32_t* ids, hipStream_t s) {
-  if (ntok <= kBucketPer * 1024 && E <= 32)
-    hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(1024), 0, s, cls, ntok, E, offsets, ids);
+hipError_t launch_bucket(const int32_t* cls, const int32_t* counts, int ntok, int E, int32_t* offsets, int32_t* ids,
+                         hipStream_t s) {
+  if (ntok <= 0) return hipSuccess;
+  if (E > 31) return hipErrorInvalidValue;
+  const dim3 grid((ntok + kBucketTok - 1) / kBucketTok);
+  const int ld = bucket_counts_ld(ntok);
+  if (E <= 16)
+    hipLaunchKernelGGL(bucket_kernel<16>, grid, dim3(kBucketTok), 0, s, cls, counts, ld, ntok, E, offsets, ids);
   else
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, s, cls, ntok, E, offsets, ids);
+    hipLaunchKernelGGL(bucket_kernel<32>, grid, dim3(kBucketTok), 0, s, cls, counts, ld, ntok, E, offsets, ids);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@
 
 namespace zaya {
 
-constexpr int kRouterTok = 16;
+constexpr int kRouterTok = kRouterTokens;
 constexpr int kRouterR = 256;
 constexpr int kRouterWaves = 8;
 constexpr int kRouterRows = kRouterR / kRouterWaves;  // fc output rows per wave
@@ -299,6 +299,12 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
     }
   }
   __syncthreads();
+  if (a.counts && (int)threadIdx.x < NC) {  // the tile's tokens of class threadIdx.x
+    int n = 0;
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) n += (tok0 + t < a.ntok && cls_s[t] == (int)threadIdx.x) ? 1 : 0;
+    a.counts[(size_t)threadIdx.x * a.counts_ld + blockIdx.x] = n;
+  }
 
   // skip tokens: out = (h + rb) * rs + rnd(rnd(hsb) * hss). The merge vectors are the
   // same for every token; the stream rows of all the tile's skip tokens are requested

@@ -84,7 +84,7 @@ int prefill_chunks_ws(const zaya_block_config* c, int S) {
 // Workspace layout of one block call.
 struct Plan {
   size_t cache_len, xn, P, vdp, y2, Q, Kw, Vw, convw, prevw, O, h, hn, logits, cls, idx, wts, offsets, ids, neurons,
-      part;
+      part, rcnt;
   size_t gpart, gpart_bytes;  // split-K partials of the few-row GEMMs
   size_t total;
 };
@@ -122,6 +122,7 @@ Plan plan_block(const zaya_block_config* c, int B, int S, int decode) {
   p.wts = take(T * A);
   p.offsets = take((size_t)(E + 1) * 4);
   p.ids = take(T * 4);
+  p.rcnt = take((size_t)(E + 1) * bucket_counts_ld((int)T) * 4);
   p.neurons = take(T * c->expert_inter * A);
   p.part = decode ? take(attn_decode_part_bytes(B, nkv, nh / nkv, d))
                   : take(attn_prefill_part_bytes(B, S, nkv, nh / nkv, d, prefill_chunks_ws(c, S)));
@@ -311,6 +312,11 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   RouterArgs<T> ra{(const T*)s_out, W(w->r_norm_g), W(w->r_W1), W(w->r_b1), W(w->r_W2), W(w->r_b2), W(w->r_Wout),
                    w->bal_bias, logits, cls, idx, wts, h, W(w->m_hsb), W(w->m_hss), W(w->m_rb), W(w->m_rs), x_out,
                    (T*)tp.routed_output, (T*)tp.mlp_output, T_, R, E, H, c->rms_eps};
+  const bool small_buckets = T_ <= 64;
+  if (!small_buckets) {
+    ra.counts = (int32_t*)(ws + p.rcnt);
+    ra.counts_ld = bucket_counts_ld(T_);
+  }
   if (rparts > 0) {
     ra.part = gpart;
     ra.kparts = rparts;
@@ -326,9 +332,8 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
   HIPCHK(tap_copy(tp.expert_weights, wts, (size_t)T_ * A));
   // a9: buckets (at most 64 tokens: formed by the gate/up kernel itself)
   HIPCHK(mark(8));
-  const bool small_buckets = T_ <= 64;
   if (!small_buckets) {
-    HIPCHK(launch_bucket(cls, T_, E, offsets, ids, st));
+    HIPCHK(launch_bucket(cls, ra.counts, T_, E, offsets, ids, st));
     HIPCHK(tap_copy(tp.bucket_offsets, offsets, (size_t)(E + 1) * 4));
     HIPCHK(tap_copy(tp.bucket_ids, ids, (size_t)T_ * 4));
   }
