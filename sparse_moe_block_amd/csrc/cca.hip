@@ -39,7 +39,9 @@ constexpr int kCcaRows = kCcaTokens + 2;  // the tile plus two tokens of history
 //   y2s[m][0 .. GC)  the two-stage conv output of token t0 + m
 // D (head_dim) and GG (query heads per KV head) are compile-time, so the per-head
 // loops unroll and the head norms' cross-lane reductions run side by side.
-template <typename T, int D, int GG, bool TWO>
+// PARTS: the decode form that sums the projection's split-K partials (a separate
+// instantiation, so the prefill form does not carry its registers).
+template <typename T, int D, int GG, bool TWO, bool PARTS>
 __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   extern __shared__ __attribute__((aligned(16))) char cca_lds[];
   const int b = blockIdx.z, g = blockIdx.y, tile = blockIdx.x;
@@ -64,16 +66,21 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   // group channel c -> global channel (column of P, row of conv_w / conv_state)
   auto gchan = [&](int c) { return c < G * d ? g * G * d + c : kcol + g * d + (c - G * d); };
 
-  // the last token's normed input becomes prev_hs: requested now, stored at the end
+  // the last token's normed input becomes prev_hs (nothing in this kernel reads prev_hs:
+  // the delayed value of the token before comes in through vdp)
   constexpr int E16 = 16 / (int)sizeof(T);
-  const bool write_prev = t_end == S && g == 0;
-  const int prev_chunks = a.H / E16;
-  u32x4 prev[4];
-  if (write_prev) {
+  if (t_end == S && g == 0) {
+    const int prev_chunks = a.H / E16;
+    u32x4 prev[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = threadIdx.x + k * (int)blockDim.x;
       if (i < prev_chunks) prev[k] = *reinterpret_cast<const u32x4*>(a.xn + ((size_t)b * S + S - 1) * a.H + i * E16);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * (int)blockDim.x;
+      if (i < prev_chunks) *reinterpret_cast<u32x4*>(a.prev_hs + (size_t)b * a.H + i * E16) = prev[k];
     }
   }
 
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         dst = GC + d / 2 + (cc - segq - segk - segv) * E16;
       }
     };
-    if (a.qkv_part) {
+    if (PARTS) {
       // the projection's split-K partials, summed in ascending order from zero and
       // rounded to T (what the pair's reduction pass would have stored in P)
       const size_t MN = (size_t)a.B * S * QR;
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       }
       for (int i = threadIdx.x; i < d / 2; i += nthr) {
         T v = Act<T>::cvt(0.f);
-        if (!fresh && a.vd_part) {
+        if (PARTS && !fresh) {
           const size_t N2 = (size_t)nkv * d / 2, MN2 = (size_t)a.B * N2;
           float acc = 0.f;
           for (int kp = 0; kp < a.kparts; ++kp) acc += a.vd_part[kp * MN2 + b * N2 + g * (d / 2) + i];
@@ -379,13 +386,6 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
       }
       cs[0] = s0;
       cs[1] = s1;
-    }
-  }
-  if (write_prev) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = threadIdx.x + k * (int)blockDim.x;
-      if (i < prev_chunks) *reinterpret_cast<u32x4*>(a.prev_hs + (size_t)b * a.H + i * E16) = prev[k];
     }
   }
 }
@@ -659,12 +659,13 @@ template <typename T, int DD, int GG>
 static hipError_t launch_cca_dg(const CcaArgs<T>& a, dim3 grid, hipStream_t s) {
   const size_t lds = cca_lds_bytes(DD, GG, (int)sizeof(T), a.conv_k == 2);
   if (a.conv_k == 2) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)cca_kernel<T, DD, GG, true>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)cca_kernel<T, DD, GG, true, false>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((cca_kernel<T, DD, GG, true>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((cca_kernel<T, DD, GG, true, false>), grid, dim3(256), lds, s, a);
   } else {
-    hipLaunchKernelGGL((cca_kernel<T, DD, GG, false>), grid, dim3(256), lds, s, a);
+    if (a.qkv_part) hipLaunchKernelGGL((cca_kernel<T, DD, GG, false, true>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((cca_kernel<T, DD, GG, false, false>), grid, dim3(256), lds, s, a);
   }
   return hipGetLastError();
 }
