@@ -422,16 +422,22 @@ def _blas_name() -> str:
         return "unknown"
 
 
+def _blas_threads() -> int:
+    """Threads the BLAS behind NumPy uses (the oracle's matmuls are the only parallel part)."""
+    try:
+        import threadpoolctl
+        return int(max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                       if i.get("user_api") == "blas"))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(cfg):
     """The CPU oracle (as it stands) on the same seeded prefill input, timed on the host:
     whole prefills repeated until about 10 s have passed (at least three when they fit);
     the value comes from the median run."""
     from oracle import zaya_oracle as O
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = _blas_threads()
     w = {k: v.float().numpy() for k, v in block_weights(cfg).items()}
     inp = block_inputs(cfg)
     x = inp["x"].numpy().astype(np.float64)
@@ -472,7 +478,7 @@ def cpu_baseline_decode(cfg, budget_s=10.0):
         if time.perf_counter() - t_all >= budget_s:
             break
     med = float(np.median(runs))
-    return {"value": round(cfg.batch / med, 1), "unit": "tokens/s", "kind": "oracle",
+    return {"value": round(cfg.batch / med, 1), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"{len(runs)} decode steps of the {cfg.batch}-sequence workload over {cfg.kv_len} cached "
                       f"tokens in {sum(runs):.1f} s; median {med:.2f} s per step"}
 
