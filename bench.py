@@ -82,9 +82,9 @@ def pack_arena(tensors, dev="cuda"):
 
 
 def expert_layout(cfg, w):
-    """Device weights in the configuration's expert layout: "act_packed" workloads run on
-    the packed copy the library makes once (weight preparation, outside any timed region)."""
-    if getattr(cfg, "expert_format", "act") != "act_packed":
+    """Device weights in the configuration's expert layout: "packed" workloads run on the
+    packed copy the library makes once (weight preparation, outside any timed region)."""
+    if getattr(cfg, "expert_layout", "rows") != "packed":
         return w
     out = Z.packed_expert_weights(cfg, w)
     torch.cuda.synchronize()

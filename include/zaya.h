@@ -49,10 +49,16 @@ enum zaya_dtype { ZAYA_F32 = 0, ZAYA_BF16 = 1 };
  * one fp32 scale per weight row: the weight is code_value * scale. A low-precision
  * deployment of the experts, like the quantized ZAYA1 bundles (the JANGTQ2 card's
  * "Quantization" section); it needs act_dtype ZAYA_BF16. */
-/* ZAYA_EXPERTS_ACT_PACKED: the act dtype, with W_gu and W_dn in the packed layout that
- * zaya_pack_experts writes (see there); the arithmetic is that of ZAYA_EXPERTS_ACT, bit for
- * bit, only the order of the weight bytes in memory differs. */
-enum zaya_expert_format { ZAYA_EXPERTS_ACT = 0, ZAYA_EXPERTS_FP8_E4M3 = 1, ZAYA_EXPERTS_ACT_PACKED = 2 };
+/* ZAYA_EXPERTS_ACT_PACKED, ZAYA_EXPERTS_FP8_E4M3_PACKED: as ZAYA_EXPERTS_ACT and
+ * ZAYA_EXPERTS_FP8_E4M3, with W_gu and W_dn in the packed layouts that zaya_pack_experts
+ * writes (see there); the arithmetic is the same bit for bit, only the order of the weight
+ * bytes in memory differs (the FP8 row scales keep their layout). */
+enum zaya_expert_format {
+  ZAYA_EXPERTS_ACT = 0,
+  ZAYA_EXPERTS_FP8_E4M3 = 1,
+  ZAYA_EXPERTS_ACT_PACKED = 2,
+  ZAYA_EXPERTS_FP8_E4M3_PACKED = 3
+};
 
 enum zaya_status {
   ZAYA_OK = 0,
@@ -298,13 +304,18 @@ int zaya_stack_forward(const zaya_stack_config* cfg, const zaya_stack_weights* w
  * group is one contiguous run. W_gu [E, 2I, H]: group j of expert e holds 16-row blocks
  * alternating gate rows 64 j + 16 b .. + 15 and up rows I + 64 j + 16 b .. + 15
  * (b = 0..3). W_dn [E, H, I]: group g holds rows 128 g .. 128 g + 127.
- * cfg: the block configuration with act-dtype experts (ZAYA_EXPERTS_ACT or
- * ZAYA_EXPERTS_ACT_PACKED; ZAYA_EDTYPE for FP8). W_gu, W_dn: row-major device inputs as in
- * zaya_block_weights. W_gu_packed, W_dn_packed: device outputs of the same byte sizes,
- * caller-owned, overlapping neither input nor each other (ZAYA_EALIAS). Enqueued on
- * stream, asynchronous; the inputs may be freed once the stream has passed the copy.
- * Blocks then run with expert_format ZAYA_EXPERTS_ACT_PACKED and the packed pointers as
- * W_gu / W_dn. */
+ * FP8 experts (E4M3 codes, one byte each) are packed for their own kernel, which streams
+ * 16 rows of 64 bytes per step: rows in blocks of 16 (the matrix's own row order), each
+ * block stored step after step (bytes 64 s .. 64 s + 63 of its 16 rows, row after row),
+ * so a step is one contiguous KiB.
+ * cfg: the block configuration; its expert_format says the element type (act dtype:
+ * ZAYA_EXPERTS_ACT or _ACT_PACKED; FP8: ZAYA_EXPERTS_FP8_E4M3 or _FP8_E4M3_PACKED). W_gu,
+ * W_dn: row-major device inputs as in zaya_block_weights. W_gu_packed, W_dn_packed: device
+ * outputs of the same byte sizes, caller-owned, overlapping neither input nor each other
+ * (ZAYA_EALIAS). Enqueued on stream, asynchronous; the inputs may be freed once the stream
+ * has passed the copy. Blocks then run with expert_format ZAYA_EXPERTS_ACT_PACKED or
+ * ZAYA_EXPERTS_FP8_E4M3_PACKED and the packed pointers as W_gu / W_dn (FP8: the same row
+ * scales). */
 int zaya_pack_experts(const zaya_block_config* cfg, const void* W_gu, const void* W_dn, void* W_gu_packed,
                       void* W_dn_packed, void* stream);
 

@@ -18,8 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzaya.so")
 
 ZAYA_F32, ZAYA_BF16 = 0, 1
-ZAYA_EXPERTS_ACT, ZAYA_EXPERTS_FP8_E4M3, ZAYA_EXPERTS_ACT_PACKED = 0, 1, 2
-_EXPERT_FORMATS = {"act": ZAYA_EXPERTS_ACT, "fp8": ZAYA_EXPERTS_FP8_E4M3, "act_packed": ZAYA_EXPERTS_ACT_PACKED}
+ZAYA_EXPERTS_ACT, ZAYA_EXPERTS_FP8_E4M3, ZAYA_EXPERTS_ACT_PACKED, ZAYA_EXPERTS_FP8_E4M3_PACKED = 0, 1, 2, 3
+# (expert_format, expert_layout) of a configuration -> the C enum
+_EXPERT_FORMATS = {("act", "rows"): ZAYA_EXPERTS_ACT, ("fp8", "rows"): ZAYA_EXPERTS_FP8_E4M3,
+                   ("act", "packed"): ZAYA_EXPERTS_ACT_PACKED, ("fp8", "packed"): ZAYA_EXPERTS_FP8_E4M3_PACKED}
 STATUS = {0: "ZAYA_OK", -1: "ZAYA_EINVAL", -2: "ZAYA_ESHAPE", -3: "ZAYA_EDTYPE", -4: "ZAYA_EWORKSPACE",
           -5: "ZAYA_ECACHE", -6: "ZAYA_EALIAS", -7: "ZAYA_EHIP"}
 
@@ -136,7 +138,7 @@ def block_config(cfg) -> BlockConfig:
                        cfg.moe_intermediate_size, cfg.router_hidden, getattr(cfg, "sliding_window", -1),
                        float(getattr(cfg, "rms_norm_eps", 1e-5)),
                        ZAYA_BF16 if cfg.act_dtype == "bf16" else ZAYA_F32,
-                       _EXPERT_FORMATS[getattr(cfg, "expert_format", "act")])
+                       _EXPERT_FORMATS[(getattr(cfg, "expert_format", "act"), getattr(cfg, "expert_layout", "rows"))])
 
 
 def block_weights(w: Mapping) -> BlockWeights:
@@ -275,7 +277,8 @@ def zaya_pack_experts(cfg, W_gu, W_dn, W_gu_packed, W_dn_packed, stream=None) ->
 
 def packed_expert_weights(cfg, w: Mapping, stream=None) -> dict:
     """A copy of the weight dict whose W_gu / W_dn are new device buffers holding the
-    packed layout of the given row-major ones (for expert_format "act_packed")."""
+    packed layout of the given row-major ones (for expert_layout "packed"; act-dtype or
+    FP8 codes as the configuration's expert_format says)."""
     import torch
     out = dict(w)
     out["W_gu"] = torch.empty_like(w["W_gu"])

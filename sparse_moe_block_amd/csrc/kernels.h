@@ -225,6 +225,11 @@ constexpr int kPackRows = 128;
 constexpr int kPackSliceBytes = 128;
 template <typename T>
 hipError_t launch_pack_experts(const T* Wgu, const T* Wdn, T* Pgu, T* Pdn, int E, int H, int I, hipStream_t s);
+// FP8 codes: rows in blocks of 16, each block stored 64-byte K step after step
+constexpr int kF8PackRows = 16;
+constexpr int kF8PackStep = 64;
+hipError_t launch_pack_experts_f8(const uint8_t* Wgu, const uint8_t* Wdn, uint8_t* Pgu, uint8_t* Pdn, int E, int H,
+                                  int I, hipStream_t s);
 template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s);
 // FP8 (E4M3) expert weights with fp32 row scales, bf16 activations

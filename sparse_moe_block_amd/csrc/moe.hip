@@ -208,6 +208,34 @@ hipError_t launch_pack_experts(const T* Wgu, const T* Wdn, T* Pgu, T* Pdn, int E
   return hipGetLastError();
 }
 
+// FP8 codes: destination 16-byte chunk i holds chunk i % 4 of the 64-byte step s of row
+// r (i / 4 % 16) of block b, expert e: source row 16 b + r, bytes 64 s + 16 (i % 4).
+__global__ __launch_bounds__(256) void pack_experts_f8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                              size_t nchunks, int rows_e, int row_bytes) {
+  const int ns = row_bytes / kF8PackStep;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nchunks; i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i & 3);
+    const int r = (int)((i >> 2) % kF8PackRows);
+    const size_t bs = i / (4 * kF8PackRows);  // (expert, block, step)
+    const int st = (int)(bs % ns);
+    const size_t eb = bs / ns;
+    const int nb = rows_e / kF8PackRows;
+    const int blk = (int)(eb % nb), e = (int)(eb / nb);
+    const size_t from = ((size_t)e * rows_e + (size_t)blk * kF8PackRows + r) * row_bytes + (size_t)st * kF8PackStep + c * 16;
+    *reinterpret_cast<u32x4*>(dst + i * 16) = *reinterpret_cast<const u32x4*>(src + from);
+  }
+}
+
+hipError_t launch_pack_experts_f8(const uint8_t* Wgu, const uint8_t* Wdn, uint8_t* Pgu, uint8_t* Pdn, int E, int H,
+                                  int I, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  if ((2 * I) % kF8PackRows || H % kF8PackRows || H % kF8PackStep || I % kF8PackStep) return hipErrorInvalidValue;
+  const size_t ngu = (size_t)E * 2 * I * H / 16, ndn = (size_t)E * H * I / 16;
+  hipLaunchKernelGGL(pack_experts_f8_kernel, dim3(2048), dim3(256), 0, s, Wgu, Pgu, ngu, 2 * I, H);
+  hipLaunchKernelGGL(pack_experts_f8_kernel, dim3(2048), dim3(256), 0, s, Wdn, Pdn, ndn, H, I);
+  return hipGetLastError();
+}
+
 template hipError_t launch_pack_experts<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, bf16_t*, int, int, int,
                                                  hipStream_t);
 template hipError_t launch_pack_experts<float>(const float*, const float*, float*, float*, int, int, int,
@@ -457,8 +485,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   const uint8_t* W = reinterpret_cast<const uint8_t*>(GATEUP ? (const void*)a.W_gu : (const void*)a.W_dn) +
                      (size_t)e * (GATEUP ? 2 * (size_t)a.I * a.H : (size_t)a.H * a.I);
   const int n_row = 64 * j + 16 * wave + r16;  // gate row (gate/up) or output row (down)
-  const uint8_t* w0 = W + (size_t)n_row * K + grp * 16;
-  const uint8_t* w1 = W + (size_t)(GATEUP ? a.I + n_row : n_row) * K + grp * 16;
+  const int up_row = GATEUP ? a.I + n_row : n_row;
+  // packed codes: the 16-row block's step s is one KiB, this lane's row at 64 r16
+  const size_t wstep = a.packed ? (size_t)kF8PackRows * kF8PackStep : (size_t)kF8PackStep;
+  auto wrow = [&](int row) -> const uint8_t* {
+    return a.packed ? W + (size_t)(row - r16) * K + r16 * kF8PackStep + grp * 16 : W + (size_t)row * K + grp * 16;
+  };
+  const uint8_t* w0 = wrow(n_row);
+  const uint8_t* w1 = wrow(up_row);
   const int nds = K / 64;
   auto wload = [](const uint8_t* p) -> u32x4 {
     if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -468,8 +502,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
   for (int p = 0; p < kF8Ahead; ++p) {
     const int s = min(p, nds - 1);
-    q0[p] = wload(w0 + (size_t)s * 64);
-    if (GATEUP) q1[p] = wload(w1 + (size_t)s * 64);
+    q0[p] = wload(w0 + (size_t)s * wstep);
+    if (GATEUP) q1[p] = wload(w1 + (size_t)s * wstep);
   }
 
   // stage the token rows (rows past the tile repeat its last row; never stored)
@@ -516,8 +550,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         }
         // refill this slot kF8Ahead steps ahead (past the end: the last step again)
         const int sn = min(s + kF8Ahead, nds - 1);
-        q0[p] = wload(w0 + (size_t)sn * 64);
-        if (GATEUP) q1[p] = wload(w1 + (size_t)sn * 64);
+        q0[p] = wload(w0 + (size_t)sn * wstep);
+        if (GATEUP) q1[p] = wload(w1 + (size_t)sn * wstep);
       }
     }
   }

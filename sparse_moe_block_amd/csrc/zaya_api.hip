@@ -40,6 +40,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t act_bytes(const zaya_block_config* c) { return c->act_dtype == ZAYA_BF16 ? 2 : 4; }
 
+bool fp8_experts(const zaya_block_config* c) {
+  return c->expert_format == ZAYA_EXPERTS_FP8_E4M3 || c->expert_format == ZAYA_EXPERTS_FP8_E4M3_PACKED;
+}
+
 int check_config(const zaya_block_config* c) {
   if (!c) return fail(ZAYA_EINVAL, "config is NULL");
   if (c->act_dtype != ZAYA_BF16 && c->act_dtype != ZAYA_F32) return fail(ZAYA_EDTYPE, "act_dtype %d", c->act_dtype);
@@ -62,10 +66,9 @@ int check_config(const zaya_block_config* c) {
   if (c->router_hidden != 256) return fail(ZAYA_ESHAPE, "router_hidden %d != 256", c->router_hidden);
   if (!(c->rms_eps > 0.f)) return fail(ZAYA_ESHAPE, "rms_eps must be > 0");
   if (!(c->rope_theta > 0.f)) return fail(ZAYA_ESHAPE, "rope_theta must be > 0");
-  if (c->expert_format != ZAYA_EXPERTS_ACT && c->expert_format != ZAYA_EXPERTS_FP8_E4M3 &&
-      c->expert_format != ZAYA_EXPERTS_ACT_PACKED)
+  if (c->expert_format < ZAYA_EXPERTS_ACT || c->expert_format > ZAYA_EXPERTS_FP8_E4M3_PACKED)
     return fail(ZAYA_EDTYPE, "expert_format %d", c->expert_format);
-  if (c->expert_format == ZAYA_EXPERTS_FP8_E4M3) {
+  if (fp8_experts(c)) {
     if (c->act_dtype != ZAYA_BF16) return fail(ZAYA_EDTYPE, "FP8 experts need act_dtype ZAYA_BF16");
     if (c->expert_inter > 4096) return fail(ZAYA_ESHAPE, "FP8 experts: expert_inter %d > 4096", c->expert_inter);
   }
@@ -143,7 +146,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 int check_weights(const zaya_block_config* c, const zaya_block_weights* w) {
   if (!w) return fail(ZAYA_EINVAL, "weights is NULL");
-  if (c->expert_format == ZAYA_EXPERTS_FP8_E4M3 && (!w->W_gu_scale || !w->W_dn_scale))
+  if (fp8_experts(c) && (!w->W_gu_scale || !w->W_dn_scale))
     return fail(ZAYA_EINVAL, "FP8 experts need W_gu_scale and W_dn_scale");
   if (c->conv_k == 2 && (!w->conv2_w || !w->conv2_b))
     return fail(ZAYA_EINVAL, "conv_k 2 needs conv2_w and conv2_b");
@@ -342,13 +345,13 @@ int run_block(const zaya_block_config* c, const zaya_block_weights* w, int B, in
                 W(w->m_rs), x_out, (T*)tp.routed_output, (T*)tp.mlp_output, T_, H, I, E};
   ma.gu_scale = w->W_gu_scale;
   ma.dn_scale = w->W_dn_scale;
-  ma.packed = c->expert_format == ZAYA_EXPERTS_ACT_PACKED;
+  ma.packed = c->expert_format == ZAYA_EXPERTS_ACT_PACKED || c->expert_format == ZAYA_EXPERTS_FP8_E4M3_PACKED;
   if (small_buckets) {
     ma.cls = cls;
     ma.offsets_out = offsets;
     ma.ids_out = ids;
   }
-  const bool f8 = c->expert_format == ZAYA_EXPERTS_FP8_E4M3;  // act is bf16 (checked)
+  const bool f8 = fp8_experts(c);  // act is bf16 (checked)
   HIPCHK(mark(9));
   if constexpr (std::is_same<T, bf16_t>::value) {
     HIPCHK(f8 ? launch_moe_gateup_f8(ma, st) : launch_moe_gateup<T>(ma, st));
@@ -623,11 +626,10 @@ int zaya_pack_experts(const zaya_block_config* cfg, const void* W_gu, const void
   g_err.clear();
   int rc = check_config(cfg);
   if (rc) return rc;
-  if (cfg->expert_format == ZAYA_EXPERTS_FP8_E4M3)
-    return fail(ZAYA_EDTYPE, "zaya_pack_experts packs act-dtype experts, not FP8 codes");
   if (!W_gu || !W_dn || !W_gu_packed || !W_dn_packed) return fail(ZAYA_EINVAL, "expert weight pointer is NULL");
   const int E = cfg->n_experts, H = cfg->hidden, I = cfg->expert_inter;
-  const size_t A = act_bytes(cfg);
+  const bool f8 = fp8_experts(cfg);
+  const size_t A = f8 ? 1 : act_bytes(cfg);
   const size_t ngu = (size_t)E * 2 * I * H * A, ndn = (size_t)E * H * I * A;
   if (overlap(W_gu_packed, ngu, W_gu, ngu) || overlap(W_gu_packed, ngu, W_dn, ndn) ||
       overlap(W_dn_packed, ndn, W_gu, ngu) || overlap(W_dn_packed, ndn, W_dn, ndn) ||
@@ -635,7 +637,9 @@ int zaya_pack_experts(const zaya_block_config* cfg, const void* W_gu, const void
     return fail(ZAYA_EALIAS, "packed expert weights overlap the row-major ones or each other");
   const hipStream_t st = (hipStream_t)stream;
   const hipError_t e =
-      cfg->act_dtype == ZAYA_BF16
+      f8 ? launch_pack_experts_f8((const uint8_t*)W_gu, (const uint8_t*)W_dn, (uint8_t*)W_gu_packed,
+                                  (uint8_t*)W_dn_packed, E, H, I, st)
+      : cfg->act_dtype == ZAYA_BF16
           ? launch_pack_experts<bf16_t>((const bf16_t*)W_gu, (const bf16_t*)W_dn, (bf16_t*)W_gu_packed,
                                         (bf16_t*)W_dn_packed, E, H, I, st)
           : launch_pack_experts<float>((const float*)W_gu, (const float*)W_dn, (float*)W_gu_packed,

@@ -299,7 +299,7 @@ def test_noalloc_decode_rejects_oversized_steps_before_any_device_call(L):
 
 
 def test_pack_experts_validation(L):
-    """zaya_pack_experts: act-dtype experts only, no NULL pointer, packed buffers that
+    """zaya_pack_experts: a known expert format, no NULL pointer, packed buffers that
     overlap neither the row-major ones nor each other. Every case fails before a launch."""
     cfg = CONFIGS["prefill"]
     E, H, I = cfg.num_experts, cfg.hidden_size, cfg.moe_intermediate_size
@@ -308,8 +308,10 @@ def test_pack_experts_validation(L):
     pgu, pdn = FAKE + ngu + ndn, FAKE + 2 * ngu + ndn
     pack = lambda c, *p: L.zaya_pack_experts(C.byref(Z.block_config(c)), *[C.c_void_p(v) if v else None for v in p],
                                              None)
-    assert pack(CONFIGS["decode_fp8"], gu, dn, pgu, pdn) == -3
-    assert "FP8" in L.zaya_last_error().decode()
+    bad = Z.block_config(cfg)
+    bad.expert_format = 7
+    assert L.zaya_pack_experts(C.byref(bad), C.c_void_p(gu), C.c_void_p(dn), C.c_void_p(pgu), C.c_void_p(pdn),
+                               None) == -3
     assert pack(cfg, gu, dn, None, pdn) == -1
     assert pack(cfg, gu, dn, dn + 4096, pdn) == -6  # packed W_gu over the row-major W_dn
     assert pack(cfg, gu, dn, pgu, pgu + ngu - 2) == -6  # the two packed buffers overlap

@@ -1,4 +1,4 @@
-"""Packed expert weights (zaya_pack_experts, expert_format ZAYA_EXPERTS_ACT_PACKED).
+"""Packed expert weights (zaya_pack_experts; ZAYA_EXPERTS_ACT_PACKED, ZAYA_EXPERTS_FP8_E4M3_PACKED).
 
 The packed layout only reorders the weight bytes: the layout itself is checked element
 by element against its definition in include/zaya.h (an index map built here from
@@ -43,7 +43,7 @@ def _pack_ref(W: torch.Tensor, rows: np.ndarray) -> torch.Tensor:
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_packed_layout_matches_its_definition(act):
     cfg = CONFIGS["tiny"].replace(name="pack_layout", act_dtype=act, num_experts=3, hidden_size=256,
-                                  moe_intermediate_size=192, expert_format="act_packed")
+                                  moe_intermediate_size=192, expert_layout="packed")
     E, H, I = cfg.num_experts, cfg.hidden_size, cfg.moe_intermediate_size
     dt = cfg.torch_dtype
     g = torch.Generator().manual_seed(3)
@@ -60,6 +60,24 @@ def test_packed_layout_matches_its_definition(act):
     assert torch.equal(Pdn.cpu().reshape(-1), ref_dn)
 
 
+def test_packed_fp8_layout_matches_its_definition():
+    """FP8 codes: rows in blocks of 16, each block stored 64-byte step after step."""
+    cfg = CONFIGS["tiny"].replace(name="pack_layout8", act_dtype="bf16", num_experts=3, hidden_size=256,
+                                  moe_intermediate_size=192, expert_format="fp8", expert_layout="packed")
+    E, H, I = cfg.num_experts, cfg.hidden_size, cfg.moe_intermediate_size
+    g = torch.Generator().manual_seed(5)
+    Wgu = torch.randint(0, 256, (E, 2 * I, H), generator=g, dtype=torch.uint8)
+    Wdn = torch.randint(0, 256, (E, H, I), generator=g, dtype=torch.uint8)
+    Pgu = torch.zeros_like(Wgu, device=DEV)
+    Pdn = torch.zeros_like(Wdn, device=DEV)
+    print(f"[gpu] pack layout fp8 E={E} H={H} I={I}", flush=True)
+    Z.zaya_pack_experts(cfg, Wgu.to(DEV), Wdn.to(DEV), Pgu, Pdn)
+    torch.cuda.synchronize()
+    ref = lambda W: W.reshape(E, W.shape[1] // 16, 16, W.shape[2] // 64, 64).permute(0, 1, 3, 2, 4).reshape(-1)
+    assert torch.equal(Pgu.cpu().reshape(-1), ref(Wgu))
+    assert torch.equal(Pdn.cpu().reshape(-1), ref(Wdn))
+
+
 def _bits(t: torch.Tensor) -> torch.Tensor:
     return t.detach().contiguous().view(torch.uint8).cpu()
 
@@ -67,7 +85,7 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
 def _same_run(cfg_rowmajor):
     """The block on row-major and on packed weights, same inputs: outputs and taps equal
     bit for bit."""
-    cfg_p = cfg_rowmajor.replace(expert_format="act_packed")
+    cfg_p = cfg_rowmajor.replace(expert_layout="packed")
     w = block_weights(cfg_rowmajor)
     inp = block_inputs(cfg_rowmajor)
     a = BlockRun(cfg_rowmajor, w_host=w, inp=inp).run()
@@ -86,12 +104,21 @@ def _same_run(cfg_rowmajor):
 
 def test_packed_prefill_bit_identical():
     # 600 tokens over 16 experts: row tiles of 128 with ragged tails, every expert group
-    _same_run(CONFIGS["prefill"].replace(name="packed_pre", batch=1, seq=600, expert_format="act"))
+    _same_run(CONFIGS["prefill"].replace(name="packed_pre", batch=1, seq=600, expert_layout="rows"))
 
 
 def test_packed_decode_bit_identical():
-    _same_run(CONFIGS["decode"].replace(name="packed_dec", kv_len=300, expert_format="act"))
+    _same_run(CONFIGS["decode"].replace(name="packed_dec", kv_len=300, expert_layout="rows"))
 
 
 def test_packed_fp32_bit_identical():
     _same_run(CONFIGS["tiny"].replace(name="packed_tiny", seq=100, batch=2))
+
+
+def test_packed_fp8_decode_bit_identical():
+    _same_run(CONFIGS["decode_fp8"].replace(name="packed_dec8", kv_len=300, expert_layout="rows"))
+
+
+def test_packed_fp8_prefill_bit_identical():
+    _same_run(CONFIGS["prefill"].replace(name="packed_pre8", batch=1, seq=600, expert_format="fp8",
+                                         expert_layout="rows"))

@@ -208,9 +208,9 @@ def cca_bound(cfg, w, xn_gpu, xn_ref, cache_len, conv_state, prev_hs, act: str):
 
 
 def pack_if_needed(cfg, w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
-    """Device weights in the expert layout the configuration names: with expert_format
-    "act_packed" the library's zaya_pack_experts lays out the row-major W_gu / W_dn."""
-    if getattr(cfg, "expert_format", "act") != "act_packed":
+    """Device weights in the expert layout the configuration names: with expert_layout
+    "packed" the library's zaya_pack_experts lays out the row-major W_gu / W_dn."""
+    if getattr(cfg, "expert_layout", "rows") != "packed":
         return w
     out = Z.packed_expert_weights(cfg, w)
     torch.cuda.synchronize()

@@ -59,10 +59,10 @@ class ZayaConfig:
     conv2_std: float = 0.02  # std of the grouped conv stage's taps and bias (conv_k == 2)
     gain_std: float = 0.0  # RMSNorm gains: 1 + N(0, gain_std); 0 = ones
     bal_bias: str = "zeros"  # "zeros", "normal", "trained", "zipf"
-    # "act": expert weights in the act dtype; "fp8": stored as E4M3 bytes + fp32 row scales;
-    # "act_packed": drawn as for "act" (row-major), the block library lays them out in its
-    # packed form before use
-    expert_format: str = "act"
+    expert_format: str = "act"  # "act" or "fp8": expert weights stored as E4M3 bytes + fp32 row scales
+    # "rows": the expert weights go to the block library row-major, as drawn; "packed": the
+    # library lays them out in its packed form (zaya_pack_experts) before the runs
+    expert_layout: str = "rows"
 
     @property
     def conv_channels(self) -> int:
@@ -89,7 +89,7 @@ class ZayaConfig:
 def _full(**kw) -> dict:
     base = dict(hidden_size=2048, num_heads=8, num_kv_heads=2, head_dim=128, rope_dim=64,
                 rope_theta=1e6, num_experts=16, moe_intermediate_size=2048, router_hidden=256,
-                act_dtype="bf16", expert_format="act_packed")
+                act_dtype="bf16", expert_layout="packed")
     base.update(kw)
     return base
 
