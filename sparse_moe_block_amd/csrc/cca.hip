@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   //    contiguous segments), the history rows from conv_state / zeros, and the conv
   //    taps. Each loop issues its loads in batches of kBatch per thread before any of
   //    them is stored, so the tile waits for memory a few times, not once per chunk.
+  //    The launch uses 256 threads.
   {
     constexpr int kBatch = 8;
     const int nthr = (int)blockDim.x;
@@ -109,6 +110,59 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         dst = GC + d / 2 + (cc - segq - segk - segv) * E16;
       }
     };
+    // The conv taps and bias of the group's channels and, for tile 0, the history rows
+    // (tokens -2, -1 of a sequence with cached tokens: q/k channels from conv_state) and
+    // the delayed value of token -1 (prev_hs @ W_vd^T): requested before the tile rows and
+    // held in registers, so all of the tile's loads are in flight together.
+    constexpr int kWSlots = ((GG + 1) * D + 255) / 256;      // channels per thread
+    constexpr int kHSlots = (2 * (GG + 1) * D + 255) / 256;  // history values per thread
+    float wv[kWSlots][4];
+#pragma unroll
+    for (int k = 0; k < kWSlots; ++k) {
+      const int gc = gchan(min((int)threadIdx.x + k * 256, GC - 1));
+      if (TWO) {  // depthwise taps (previous, current) and bias: the new state's slot 1
+        wv[k][0] = Act<T>::tof(a.conv_w[gc * 2 + 0]);
+        wv[k][1] = Act<T>::tof(a.conv_w[gc * 2 + 1]);
+        wv[k][2] = Act<T>::tof(a.conv_b[gc]);
+        wv[k][3] = 0.f;
+      } else {
+        wv[k][0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
+        wv[k][1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
+        wv[k][2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
+        wv[k][3] = Act<T>::tof(a.conv_b[gc]);
+      }
+    }
+    T hv[kHSlots];
+    float vdv = 0.f;
+    if (t0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kHSlots; ++k) {
+        const int i = min((int)threadIdx.x + k * 256, 2 * GC - 1);
+        const int rr = i / GC, c = i % GC;
+        // kernel 3: rows -2, -1 are slots 0, 1. Two stages: row -1 is slot 0 (the input
+        // one token back), used for the new state
+        const bool none = fresh || (TWO && rr == 0);
+        hv[k] = none ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + (TWO ? 0 : rr)];
+      }
+      if ((int)threadIdx.x < d / 2 && !fresh) {
+        const int i = threadIdx.x;
+        if (PARTS) {  // the delayed value's split-K partials, summed in ascending order from zero
+          const size_t N2 = (size_t)nkv * d / 2, MN2 = (size_t)a.B * N2;
+          const float* vp = a.vd_part + b * N2 + g * (d / 2) + i;
+          for (int k0 = 0; k0 < a.kparts; k0 += 8) {
+            float w8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w8[k] = k0 + k < a.kparts ? vp[(k0 + k) * MN2] : 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (k0 + k < a.kparts) vdv += w8[k];
+          }
+          vdv = Act<T>::tof(Act<T>::cvt(vdv));
+        } else {
+          vdv = Act<T>::tof(a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + i]);
+        }
+      }
+    }
     if (PARTS) {
       // the projection's split-K partials, summed in ascending order from zero and
       // rounded to T (what the pair's reduction pass would have stored in P)
@@ -178,64 +232,21 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
         }
       }
     }
-    // history (tokens -2, -1 of a sequence with cached tokens): q/k channels from
-    // conv_state, the delayed value from prev_hs @ W_vd^T
-    if (t0 == 0) {
-      for (int i0 = threadIdx.x; i0 < 2 * GC; i0 += kBatch * nthr) {
-        T hv[kBatch];
+    // the held taps, history rows and delayed value go to LDS
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const int i = i0 + k * nthr;
-          const int rr = i / GC, c = i % GC;
-          // kernel 3: rows -2, -1 are slots 0, 1. Two stages: row -1 is slot 0 (the input
-          // one token back), used for the new state
-          const bool none = fresh || i >= 2 * GC || (TWO && rr == 0);
-          hv[k] = none ? Act<T>::cvt(0.f) : a.conv_state[((size_t)b * a.C + gchan(c)) * 2 + (TWO ? 0 : rr)];
-        }
+    for (int k = 0; k < kWSlots; ++k) {
+      const int c = (int)threadIdx.x + k * 256;
+      if (c < GC)
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const int i = i0 + k * nthr;
-          if (i < 2 * GC) xs[(i / GC) * ROWE + i % GC] = hv[k];
-        }
-      }
-      for (int i = threadIdx.x; i < d / 2; i += nthr) {
-        T v = Act<T>::cvt(0.f);
-        if (PARTS && !fresh) {
-          const size_t N2 = (size_t)nkv * d / 2, MN2 = (size_t)a.B * N2;
-          float acc = 0.f;
-          for (int kp = 0; kp < a.kparts; ++kp) acc += a.vd_part[kp * MN2 + b * N2 + g * (d / 2) + i];
-          v = Act<T>::cvt(acc);
-        } else if (!fresh) {
-          v = a.vdp[(size_t)b * (nkv * d / 2) + g * (d / 2) + i];
-        }
-        xs[1 * ROWE + GC + d / 2 + i] = v;
-      }
+        for (int q = 0; q < 4; ++q) wsm[c * 4 + q] = wv[k][q];
     }
-    for (int c0 = threadIdx.x; c0 < GC; c0 += 2 * nthr) {
-      float wv[2][4];
+    if (t0 == 0) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int c = c0 + k * nthr;
-        const int gc = gchan(min(c, GC - 1));
-        if (TWO) {  // depthwise taps (previous, current) and bias: the new state's slot 1
-          wv[k][0] = Act<T>::tof(a.conv_w[gc * 2 + 0]);
-          wv[k][1] = Act<T>::tof(a.conv_w[gc * 2 + 1]);
-          wv[k][2] = Act<T>::tof(a.conv_b[gc]);
-          wv[k][3] = 0.f;
-        } else {
-          wv[k][0] = Act<T>::tof(a.conv_w[gc * 3 + 0]);
-          wv[k][1] = Act<T>::tof(a.conv_w[gc * 3 + 1]);
-          wv[k][2] = Act<T>::tof(a.conv_w[gc * 3 + 2]);
-          wv[k][3] = Act<T>::tof(a.conv_b[gc]);
-        }
+      for (int k = 0; k < kHSlots; ++k) {
+        const int i = (int)threadIdx.x + k * 256;
+        if (i < 2 * GC) xs[(i / GC) * ROWE + i % GC] = hv[k];
       }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int c = c0 + k * nthr;
-        if (c < GC)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) wsm[c * 4 + q] = wv[k][q];
-      }
+      if ((int)threadIdx.x < d / 2) xs[1 * ROWE + GC + d / 2 + threadIdx.x] = Act<T>::cvt(vdv);
     }
   }
   __syncthreads();
