@@ -939,36 +939,59 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnArgs<T> a, 
   const int g = h / G, w = h % G;
   const float* base = part + (((size_t)b * a.nkv + g) * nchunk * G + w) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
-  __shared__ float m_s[128], sc_s[128];
-  __shared__ float M_s, L_s;
-  for (int c = threadIdx.x; c < nchunk; c += 64) m_s[c] = base[c * stride + D];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, m_s[c]);
-    M_s = M;
+  constexpr int DPL = D / 64;  // dims per lane
+  constexpr int kBatch = 32;   // chunks whose partial outputs are requested at once
+  __shared__ float sc_s[kDecChunksMax];
+  // every load the merge needs before its first use: the chunk maxima and sums of this
+  // lane's chunks (c = lane, lane + 64) and the first kBatch chunks' outputs
+  float m2[2], l2[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = (int)threadIdx.x + 64 * k;
+    m2[k] = c < nchunk ? base[c * stride + D] : -INFINITY;
+    l2[k] = c < nchunk ? base[c * stride + D + 1] : 0.f;
   }
-  __syncthreads();
+  const float* pl = base + threadIdx.x * DPL;
+  float ov[kBatch][DPL];
+#pragma unroll
+  for (int c = 0; c < kBatch; ++c)
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) ov[c][j] = c < nchunk ? pl[c * stride + j] : 0.f;
+  float M = fmaxf(m2[0], m2[1]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   float lpart = 0.f;
-  for (int c = threadIdx.x; c < nchunk; c += 64) {
-    const float sc = m_s[c] == -INFINITY ? 0.f : exp2f(m_s[c] - M_s);
-    sc_s[c] = sc;
-    lpart += sc * base[c * stride + D + 1];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = (int)threadIdx.x + 64 * k;
+    if (c < nchunk) {
+      const float sc = m2[k] == -INFINITY ? 0.f : exp2f(m2[k] - M);
+      sc_s[c] = sc;
+      lpart += sc * l2[k];
+    }
   }
-  lpart = wave_sum(lpart);
-  if (threadIdx.x == 0) L_s = lpart;
+  const float L = wave_sum(lpart);
   __syncthreads();
-  float acc[D / 64];
+  float acc[DPL];
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < nchunk; ++c) {
-    const float sc = sc_s[c];
-    const float* pc = base + c * stride + threadIdx.x * (D / 64);
+  for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) acc[j] += sc * pc[j];
+  for (int c = 0; c < kBatch; ++c)
+    if (c < nchunk)
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[j] += sc_s[c] * ov[c][j];
+  for (int c0 = kBatch; c0 < nchunk; c0 += kBatch) {  // further chunks, kBatch loads at a time
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c)
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) ov[c][j] = c0 + c < nchunk ? pl[(c0 + c) * stride + j] : 0.f;
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c)
+      if (c0 + c < nchunk)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j] += sc_s[c0 + c] * ov[c][j];
   }
-  const float inv = L_s > 0.f ? 1.f / L_s : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   T* orow = a.O + ((size_t)b * a.nh + h) * D;
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) orow[threadIdx.x * (D / 64) + j] = Act<T>::cvt(acc[j] * inv);

@@ -98,8 +98,10 @@ hipError_t launch_rmsnorm_stream(const float* x, const T* g, T* out, int rows, i
 // attention merge exactly as the o_proj merge epilogue (attention_output =
 // rnd(rnd(o + hsb) * hss); h = f32(f32(x + rb) * rs) + attention_output), then the
 // post-attention RMSNorm of h as rmsnorm_stream_kernel computes it (the sum of squares
-// reduced over the workgroup). Thread t owns columns 4t + 1024 i .. +3.
-template <typename T>
+// reduced over the workgroup). Thread t owns columns 4t + 1024 i .. +3, i < NG = H / 1024
+// rounded up. Every load is issued before the first is used: the row's stream values,
+// the merge vectors and the norm gain, then the partials, eight parts at a time.
+template <typename T, int NG>
 __global__ __launch_bounds__(256) void merge_norm_parts_kernel(const float* __restrict__ part, int kparts, int rows,
                                                                int H, const float* __restrict__ x,
                                                                const T* __restrict__ hsb, const T* __restrict__ hss,
@@ -107,11 +109,10 @@ __global__ __launch_bounds__(256) void merge_norm_parts_kernel(const float* __re
                                                                float* __restrict__ h, T* __restrict__ a_tap,
                                                                const T* __restrict__ g2, T* __restrict__ hn,
                                                                float eps) {
-  constexpr int NG = 4;  // H <= 4096
   __shared__ float red[4];
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float o[NG][4], xs[NG][4], b1[NG][4], s1[NG][4], b2[NG][4], s2[NG][4];
+  float o[NG][4], xs[NG][4], b1[NG][4], s1[NG][4], b2[NG][4], s2[NG][4], gv[NG][4];
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int n = min((int)threadIdx.x * 4 + i * 1024, H - 4);  // clamped: columns past H are never stored
@@ -122,16 +123,23 @@ __global__ __launch_bounds__(256) void merge_norm_parts_kernel(const float* __re
     load4(hss + n, s1[i]);
     load4(rb + n, b2[i]);
     load4(rs + n, s2[i]);
+    load4(g2 + n, gv[i]);
   }
-#pragma unroll 2
-  for (int kp = 0; kp < kparts; ++kp) {
-    float w[NG][4];
+  for (int k0 = 0; k0 < kparts; k0 += 8) {  // summed in part order from zero
+    float w[8][NG][4];
 #pragma unroll
-    for (int i = 0; i < NG; ++i) load4(part + ((size_t)kp * rows + row) * H + min((int)threadIdx.x * 4 + i * 1024, H - 4), w[i]);
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < kparts)
 #pragma unroll
-    for (int i = 0; i < NG; ++i)
+        for (int i = 0; i < NG; ++i)
+          load4(part + ((size_t)(k0 + k) * rows + row) * H + min((int)threadIdx.x * 4 + i * 1024, H - 4), w[k][i]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[i][c] += w[i][c];
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < kparts)
+#pragma unroll
+        for (int i = 0; i < NG; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[i][c] += w[k][i][c];
   }
   float v[NG][4];
   float ss = 0.f;
@@ -164,10 +172,9 @@ __global__ __launch_bounds__(256) void merge_norm_parts_kernel(const float* __re
   for (int i = 0; i < NG; ++i) {
     const int n = (int)threadIdx.x * 4 + i * 1024;
     if (n >= H) continue;
-    float gv[4], out[4];
-    load4(g2 + n, gv);
+    float out[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) out[c] = Act<T>::rnd(gv[c] * Act<T>::rnd(v[i][c] * inv));
+    for (int c = 0; c < 4; ++c) out[c] = Act<T>::rnd(gv[i][c] * Act<T>::rnd(v[i][c] * inv));
     store4(hn + (size_t)row * H + n, out);
   }
 }
@@ -178,8 +185,16 @@ hipError_t launch_merge_norm_parts(const float* part, int kparts, int rows, int 
                                    float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (H > 4096 || H % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((merge_norm_parts_kernel<T>), dim3(rows), dim3(256), 0, s, part, kparts, rows, H, x, hsb, hss, rb,
-                     rs, h, a_tap, g2, hn, eps);
+  switch ((H + 1023) / 1024) {
+#define ZAYA_MNP_CASE(n)                                                                                          \
+  case n:                                                                                                         \
+    hipLaunchKernelGGL((merge_norm_parts_kernel<T, n>), dim3(rows), dim3(256), 0, s, part, kparts, rows, H, x, hsb, \
+                       hss, rb, rs, h, a_tap, g2, hn, eps);                                                       \
+    break;
+    ZAYA_MNP_CASE(1) ZAYA_MNP_CASE(2) ZAYA_MNP_CASE(3) ZAYA_MNP_CASE(4)
+#undef ZAYA_MNP_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

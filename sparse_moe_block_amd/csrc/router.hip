@@ -155,51 +155,28 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
   const int r16 = lane & 15, grp = lane >> 4;
   const int E = a.E, NC = a.E + 1;
 
-  // All global reads, in the order they are needed: the router state rows (wave w
-  // normalizes tokens 2w, 2w+1; lane owns 4 consecutive values) and the norm gain, the
-  // biases and balancing biases, then the weight fragments of fc1, fc2 and out_proj
-  // (waves 0 and 1: classes 16 w .. 16 w + 15; rows past the last class repeat it and
-  // are discarded).
+  // The global reads the norm needs are issued before the first is used: the router
+  // state inputs of this wave's tokens 2w, 2w+1 (lane owns 4 consecutive values; with
+  // partials, their loads and the bias, state scale and carried state), the norm gain,
+  // the biases and balancing biases. No store comes between them, so none waits for
+  // another. The out_proj fragments (waves 0 and 1: classes 16 w .. 16 w + 15; rows past
+  // the last class repeat it and are discarded) follow.
   float v[2][4], g[4];
+  float bb[4], sc[4], st[2][4];
+  const bool part = a.part != nullptr, carry = part && a.s_in != nullptr;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int tok = tok0 + wave * 2 + tt;
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[tt][c] = 0.f;
-    if (tok < a.ntok) {
-      if (a.part) {
-        // u = the down-projection's partials summed in ascending order from zero, then
-        // rnd(+ bias) and, with a carried state, rnd(u + rnd(rss * s_in))
-        // (eight parts' loads issued at once, then summed in order)
-        const size_t MN = (size_t)a.ntok * kRouterR;
-        const float* pp = a.part + (size_t)tok * kRouterR + lane * 4;
-        for (int k0 = 0; k0 < a.kparts; k0 += 8) {
-          float w[8][4];
+  if (part) {
+    load4(a.bd + lane * 4, bb);
+    if (carry) load4(a.rss + lane * 4, sc);
+  }
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (k0 + k < a.kparts) load4(pp + (k0 + k) * MN, w[k]);
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (k0 + k < a.kparts)
-#pragma unroll
-              for (int c = 0; c < 4; ++c) v[tt][c] += w[k][c];
-        }
-        float bb[4];
-        load4(a.bd + lane * 4, bb);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[tt][c] = Act<T>::rnd(v[tt][c] + bb[c]);
-        if (a.s_in) {
-          float sc[4], st[4];
-          load4(a.rss + lane * 4, sc);
-          load4(a.s_in + (size_t)tok * kRouterR + lane * 4, st);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[tt][c] = Act<T>::rnd(v[tt][c] + Act<T>::rnd(sc[c] * st[c]));
-        }
-        store4(a.u_out + (size_t)tok * kRouterR + lane * 4, v[tt]);
-      } else {
-        load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
-      }
-    }
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tok = min(tok0 + wave * 2 + tt, a.ntok - 1);  // rows past the end: the last, never stored
+    if (!part) load4(a.u + (size_t)tok * kRouterR + lane * 4, v[tt]);
+    else if (carry) load4(a.s_in + (size_t)tok * kRouterR + lane * 4, st[tt]);
   }
   load4(a.norm_g + lane * 4, g);
   RouterFcFrags<T> w1, w2;
@@ -207,7 +184,42 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
   w2.load_bias(a.b2);
   const float bb1 = r16 < NC ? a.bal_bias[r16] : 0.f;
   const float bb2 = 16 + r16 < NC ? a.bal_bias[16 + r16] : 0.f;
+  if (part) {
+    // u = the down-projection's partials summed in ascending order from zero, then
+    // rnd(+ bias) and, with a carried state, rnd(u + rnd(rss * s_in)); the partials of
+    // both tokens requested together, four parts per token at a time
+    const size_t MN = (size_t)a.ntok * kRouterR;
+    const float* pp[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) pp[tt] = a.part + (size_t)min(tok0 + wave * 2 + tt, a.ntok - 1) * kRouterR + lane * 4;
+    for (int k0 = 0; k0 < a.kparts; k0 += 4) {
+      float w[2][4][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k0 + k < a.kparts) load4(pp[tt] + (k0 + k) * MN, w[tt][k]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k0 + k < a.kparts)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[tt][c] += w[tt][k][c];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = tok0 + wave * 2 + tt;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[tt][c] = Act<T>::rnd(v[tt][c] + bb[c]);
+      if (carry)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[tt][c] = Act<T>::rnd(v[tt][c] + Act<T>::rnd(sc[c] * st[tt][c]));
+      if (tok < a.ntok) store4(a.u_out + (size_t)tok * kRouterR + lane * 4, v[tt]);
+    }
+  }
   if constexpr (!kLds) w1.load(a.W1);  // fp32: fragments straight from memory, fc2's after fc1
+  // out_proj fragments (needed only after fc2, so their loads may wait behind the state's)
   typename Mfma<T>::frag wo[kRouterR / 32];
   if (wave < 2) {
     const int c = min(wave * 16 + r16, NC - 1);
