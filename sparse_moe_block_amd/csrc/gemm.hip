@@ -14,10 +14,25 @@
 
 namespace zaya {
 
+// Epilogues in the form GemmTile::epilogue_loaded takes (every read issued before the
+// first result): Row / Col / Elem hold what is read per row, per 4-column group and per
+// (row, group); m and n are global here (the kernel adds the tile origin).
+struct EpiNone {};
+
 template <typename T>
 struct EpiStore {
   T* C;
   int ldc;
+  using Row = EpiNone;
+  using Col = EpiNone;
+  using Elem = EpiNone;
+  __device__ __forceinline__ void load_row(int, Row&) const {}
+  __device__ __forceinline__ void load_col(int, Col&) const {}
+  __device__ __forceinline__ void load_elem(int, int, const Row&, Elem&) const {}
+  __device__ __forceinline__ void apply(int m, int n, const float* v, const Row&, const Col&, const Elem&) const {
+    store4(C + (size_t)m * ldc + n, v);
+  }
+  // split-K reduction pass: one group at a time
   __device__ __forceinline__ void operator()(int m, int n, const float* v) const { store4(C + (size_t)m * ldc + n, v); }
 };
 
@@ -28,21 +43,40 @@ struct EpiMerge {
   float* h;
   T* a_tap;
   int H;
-  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
-    float xs[4], b1[4], s1[4], b2[4], s2[4], a[4], o[4];
-    load4(x + (size_t)m * H + n, xs);
-    load4(hsb + n, b1);
-    load4(hss + n, s1);
-    load4(rb + n, b2);
-    load4(rs + n, s2);
+  using Row = EpiNone;
+  struct Col {
+    float b1[4], s1[4], b2[4], s2[4];
+  };
+  struct Elem {
+    float xs[4];
+  };
+  __device__ __forceinline__ void load_row(int, Row&) const {}
+  __device__ __forceinline__ void load_col(int n, Col& c) const {
+    load4(hsb + n, c.b1);
+    load4(hss + n, c.s1);
+    load4(rb + n, c.b2);
+    load4(rs + n, c.s2);
+  }
+  __device__ __forceinline__ void load_elem(int m, int n, const Row&, Elem& e) const {
+    load4(x + (size_t)m * H + n, e.xs);
+  }
+  __device__ __forceinline__ void apply(int m, int n, const float* v, const Row&, const Col& c, const Elem& e) const {
+    float a[4], o[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float oc = Act<T>::rnd(v[c]);
-      a[c] = Act<T>::rnd(Act<T>::rnd(oc + b1[c]) * s1[c]);
-      o[c] = fadd(fmul(fadd(xs[c], b2[c]), s2[c]), a[c]);
+    for (int q = 0; q < 4; ++q) {
+      const float oc = Act<T>::rnd(v[q]);
+      a[q] = Act<T>::rnd(Act<T>::rnd(oc + c.b1[q]) * c.s1[q]);
+      o[q] = fadd(fmul(fadd(e.xs[q], c.b2[q]), c.s2[q]), a[q]);
     }
     store4(h + (size_t)m * H + n, o);
     if (a_tap) store4(a_tap + (size_t)m * H + n, a);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    Col c;
+    Elem e;
+    load_col(n, c);
+    load_elem(m, n, Row{}, e);
+    apply(m, n, v, Row{}, c, e);
   }
 };
 
@@ -53,19 +87,54 @@ struct EpiRouterIn {
   const T* s_in;  // NULL: block-0 semantics
   T* u;
   int R;
-  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
-    float bb[4], o[4];
-    load4(b + n, bb);
+  using Row = EpiNone;
+  struct Col {
+    float bb[4], sc[4];
+  };
+  struct Elem {
+    float st[4];
+  };
+  __device__ __forceinline__ void load_row(int, Row&) const {}
+  __device__ __forceinline__ void load_col(int n, Col& c) const {
+    load4(b + n, c.bb);
+    if (s_in) load4(rss + n, c.sc);
+  }
+  __device__ __forceinline__ void load_elem(int m, int n, const Row&, Elem& e) const {
+    if (s_in) load4(s_in + (size_t)m * R + n, e.st);
+  }
+  __device__ __forceinline__ void apply(int m, int n, const float* v, const Row&, const Col& c, const Elem& e) const {
+    float o[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(v[c] + bb[c]);
-    if (s_in) {
-      float sc[4], st[4];
-      load4(rss + n, sc);
-      load4(s_in + (size_t)m * R + n, st);
+    for (int q = 0; q < 4; ++q) o[q] = Act<T>::rnd(v[q] + c.bb[q]);
+    if (s_in)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = Act<T>::rnd(o[c] + Act<T>::rnd(sc[c] * st[c]));
-    }
+      for (int q = 0; q < 4; ++q) o[q] = Act<T>::rnd(o[q] + Act<T>::rnd(c.sc[q] * e.st[q]));
     store4(u + (size_t)m * R + n, o);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    Col c;
+    Elem e;
+    load_col(n, c);
+    load_elem(m, n, Row{}, e);
+    apply(m, n, v, Row{}, c, e);
+  }
+};
+
+// Tile-local indices shifted to the tile's origin for an epilogue of global indices.
+template <class Epi>
+struct EpiAt {
+  const Epi& epi;
+  int m0, n0;
+  using Row = typename Epi::Row;
+  using Col = typename Epi::Col;
+  using Elem = typename Epi::Elem;
+  __device__ __forceinline__ void load_row(int m, Row& r) const { epi.load_row(m0 + m, r); }
+  __device__ __forceinline__ void load_col(int n, Col& c) const { epi.load_col(n0 + n, c); }
+  __device__ __forceinline__ void load_elem(int m, int n, const Row& r, Elem& e) const {
+    epi.load_elem(m0 + m, n0 + n, r, e);
+  }
+  __device__ __forceinline__ void apply(int m, int n, const float* v, const Row& r, const Col& c, const Elem& e) const {
+    epi.apply(m0 + m, n0 + n, v, r, c, e);
   }
 };
 
@@ -82,9 +151,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   t.set_a([&](int r) -> const T* { return A + (size_t)min(m0 + r, M - 1) * lda; });
   t.set_b([&](int r) -> const T* { return B + (size_t)min(n0 + r, N - 1) * ldb; });
   t.run(smem, K / Tile::kBK);
-  t.epilogue([&](int m, int n, const float* v) {
-    if (m0 + m < M && n0 + n < N) epi(m0 + m, n0 + n, v);
-  });
+  t.epilogue_loaded(EpiAt<Epi>{epi, m0, n0}, min(BM, M - m0), min(BN, N - n0));
 }
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>

@@ -189,6 +189,55 @@ struct GemmTile {
     if (k0 + 1 < nk) step(lds, k0 + 1, nk, s2);
   }
 
+  // Epilogue with loads: every global read the epilogue needs is issued before the first
+  // result is computed (a memory round trip or two per workgroup instead of one per
+  // group). Epi provides Row (values per row, loaded first: what the other loads index
+  // by), Col (per 4-column group) and Elem (per row and 4-column group) with
+  // load_row(m, Row&), load_col(n, Col&), load_elem(m, n, Row, Elem&) and
+  // apply(m, n, v[4], Row, Col, Elem); m and n are local to the tile. Rows m >= rows and
+  // column groups n >= cols do not exist: they read row 0's / column 0's values and store
+  // nothing.
+  template <class Epi>
+  __device__ __forceinline__ void epilogue_loaded(const Epi& epi, int rows, int cols = BN) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    typename Epi::Row row[kTM];
+    typename Epi::Col col[kTN];
+    typename Epi::Elem el[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int m = wm * kTM * 16 + i * 16 + (lane & 15);
+      epi.load_row(m < rows ? m : 0, row[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int n = wn * kTN * 16 + j * 16 + (lane >> 4) * 4;
+      epi.load_col(n < cols ? n : 0, col[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int m = wm * kTM * 16 + i * 16 + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int n = wn * kTN * 16 + j * 16 + (lane >> 4) * 4;
+        epi.load_elem(m < rows ? m : 0, n < cols ? n : 0, row[i], el[i][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int m = wm * kTM * 16 + i * 16 + (lane & 15);
+      if (m >= rows) continue;
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int n = wn * kTN * 16 + j * 16 + (lane >> 4) * 4;
+        if (n >= cols) continue;
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        epi.apply(m, n, v, row[i], col[j], el[i][j]);
+      }
+    }
+  }
+
   // Calls f(m_local, n_local, v[4]) for every 4-column group this lane holds;
   // n_local is the first of the four consecutive columns.
   template <class F>

@@ -346,6 +346,54 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   }
 }
 
+// Down-projection epilogue: y = rnd(sum), routed = rnd(w * y), mlp = rnd(rnd(routed + hsb)
+// * hss), out = f32(f32(h + rb) * rs) + mlp, for the item's token rows (bucket order) and
+// output columns n0 + n. The row's token and weight are read first, then the stream rows
+// and the merge vectors, all before the first result.
+template <typename T>
+struct EpiDownMerge {
+  const MoeArgs<T>& a;
+  int base, n0;
+  struct Row {
+    int tok;
+    float w;
+  };
+  struct Col {
+    float b1[4], s1[4], b2[4], s2[4];
+  };
+  struct Elem {
+    float hv[4];
+  };
+  __device__ __forceinline__ void load_row(int m, Row& r) const {
+    r.tok = a.ids[base + m];
+    r.w = Act<T>::tof(a.wts[r.tok]);
+  }
+  __device__ __forceinline__ void load_col(int nl, Col& c) const {
+    const int n = n0 + nl;
+    load4(a.hsb + n, c.b1);
+    load4(a.hss + n, c.s1);
+    load4(a.rb + n, c.b2);
+    load4(a.rs + n, c.s2);
+  }
+  __device__ __forceinline__ void load_elem(int, int nl, const Row& r, Elem& e) const {
+    load4(a.h + (size_t)r.tok * a.H + n0 + nl, e.hv);
+  }
+  __device__ __forceinline__ void apply(int, int nl, const float* v, const Row& r, const Col& c, const Elem& e) const {
+    const int n = n0 + nl;
+    float ro[4], mo[4], o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float y = Act<T>::rnd(v[q]);
+      ro[q] = Act<T>::rnd(r.w * y);
+      mo[q] = Act<T>::rnd(Act<T>::rnd(ro[q] + c.b1[q]) * c.s1[q]);
+      o[q] = fadd(fmul(fadd(e.hv[q], c.b2[q]), c.s2[q]), mo[q]);
+    }
+    store4(a.out + (size_t)r.tok * a.H + n, o);
+    if (a.routed_tap) store4(a.routed_tap + (size_t)r.tok * a.H + n, ro);
+    if (a.mlp_tap) store4(a.mlp_tap + (size_t)r.tok * a.H + n, mo);
+  }
+};
+
 template <typename T, int BM, int WM, int WN, int BN = 128>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
@@ -369,28 +417,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
     t.set_b([&](int r) -> const T* { return Wd + (size_t)(n0 + r) * a.I; });
   }
   t.run(smem, a.I / Tile::kBK);
-  t.epilogue([&](int m, int nl, const float* v) {
-    if (m >= rows) return;
-    const int tok = a.ids[base + m];
-    const int n = n0 + nl;
-    const float w = Act<T>::tof(a.wts[tok]);
-    float hv[4], b1[4], s1[4], b2[4], s2[4], ro[4], mo[4], o[4];
-    load4(a.h + (size_t)tok * a.H + n, hv);
-    load4(a.hsb + n, b1);
-    load4(a.hss + n, s1);
-    load4(a.rb + n, b2);
-    load4(a.rs + n, s2);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float y = Act<T>::rnd(v[c]);
-      ro[c] = Act<T>::rnd(w * y);
-      mo[c] = Act<T>::rnd(Act<T>::rnd(ro[c] + b1[c]) * s1[c]);
-      o[c] = fadd(fmul(fadd(hv[c], b2[c]), s2[c]), mo[c]);
-    }
-    store4(a.out + (size_t)tok * a.H + n, o);
-    if (a.routed_tap) store4(a.routed_tap + (size_t)tok * a.H + n, ro);
-    if (a.mlp_tap) store4(a.mlp_tap + (size_t)tok * a.H + n, mo);
-  });
+  t.epilogue_loaded(EpiDownMerge<T>{a, base, n0}, rows);
 }
 
 template <typename T, int BM, int WM, int WN, int BN = 128>
