@@ -91,15 +91,22 @@ struct GemmTile {
     }
   }
 
-  __device__ __forceinline__ void load_slice(int kt, u32x4* ra, u32x4* rb) const {
-    const size_t off = (size_t)kt * kRowBytes, boff = (size_t)kt * bstride;
+  __device__ __forceinline__ void load_a(int kt, u32x4* ra) const {
+    const size_t off = (size_t)kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + off);
+  }
+  __device__ __forceinline__ void load_b(int kt, u32x4* rb) const {
+    const size_t boff = (size_t)kt * bstride;
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
       if constexpr (STREAM_B) rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pb[i] + boff));
       else rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + boff);
     }
+  }
+  __device__ __forceinline__ void load_slice(int kt, u32x4* ra, u32x4* rb) const {
+    load_a(kt, ra);
+    load_b(kt, rb);
   }
 
   __device__ __forceinline__ static void store_slice(char* buf, const u32x4* ra, const u32x4* rb) {
@@ -173,9 +180,14 @@ struct GemmTile {
   __device__ __forceinline__ void run(char* lds, int nk) {
     zero_acc();
     Stage s0, s1, s2;
-    load_slice(0, s0.a, s0.b);
-    load_slice(min(1, nk - 1), s1.a, s1.b);
-    load_slice(min(2, nk - 1), s2.a, s2.b);
+    // B rows first: their addresses never wait on a gather (A's rows may be token rows
+    // found through the bucket ids)
+    load_b(0, s0.b);
+    load_b(min(1, nk - 1), s1.b);
+    load_b(min(2, nk - 1), s2.b);
+    load_a(0, s0.a);
+    load_a(min(1, nk - 1), s1.a);
+    load_a(min(2, nk - 1), s2.a);
     store_slice(lds, s0.a, s0.b);
     load_slice(min(3, nk - 1), s0.a, s0.b);
     __syncthreads();

@@ -255,27 +255,36 @@ constexpr bool kStreamFewRows = true;
 // items (the grid is sized for the worst case on the host).
 __device__ __forceinline__ bool moe_item(const int32_t* __restrict__ off, int E, int BM, int ntn, int& e_out,
                                          int& r0_out, int& n_out, int& nt_out) {
-  int tiles = 0;
-  for (int e = 0; e < E; ++e) tiles += (off[e + 1] - off[e] + BM - 1) / BM;
+  // Every wave finds the item on its own: lane e < E reads offsets e and e + 1 (one
+  // memory round trip; the offsets may live in LDS or in global memory), the row-tile
+  // counts are scanned across lanes, and the expert holding the item is the first lane
+  // whose running tile count passes it. E < 64 (checked by the host).
+  const int lane = threadIdx.x & 63;
+  const int o0 = off[min(lane, E)], o1 = off[min(lane + 1, E)];
+  const int n = lane < E ? o1 - o0 : 0;
+  const int mt = (n + BM - 1) / BM;
+  int incl = mt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const int tiles = __shfl(incl, 63, 64);
   const int n_real = tiles * ntn;
   const int per = (n_real + 7) / 8;
   const int k = (int)blockIdx.x / 8;
   if (k >= per) return false;
   int item = (int)(blockIdx.x % 8) * per + k;
   if (item >= n_real) return false;
-  for (int e = 0; e < E; ++e) {
-    const int n = off[e + 1] - off[e];
-    const int mt = (n + BM - 1) / BM;
-    if (item < mt * ntn) {
-      e_out = e;
-      nt_out = item / mt;
-      r0_out = (item % mt) * BM;
-      n_out = n;
-      return true;
-    }
-    item -= mt * ntn;
-  }
-  return false;
+  const unsigned long long past = __ballot(lane < E && incl * ntn > item);
+  const int e = __ffsll((long long)past) - 1;
+  const int mt_e = __shfl(mt, e, 64);
+  item -= (__shfl(incl, e, 64) - mt_e) * ntn;
+  e_out = e;
+  nt_out = item / mt_e;
+  r0_out = (item % mt_e) * BM;
+  n_out = __shfl(n, e, 64);
+  return true;
 }
 
 // Grid for a grouped GEMM: an upper bound on the items, rounded to the 8 XCDs.
@@ -307,7 +316,6 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   const int base = off[e] + r0;
   const int rows = min(BM, n_e - r0);
   Tile t;
-  t.set_a([&](int r) -> const T* { return a.hn + (size_t)ids[base + min(r, rows - 1)] * a.H; });
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
   if (a.packed) {  // the item's 128 rows are packed group j, in the same row order
     static_assert(BN == kPackRows, "a gate/up item is one packed row group");
@@ -321,6 +329,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
       return Wg + (size_t)row * a.H;
     });
   }
+  t.set_a([&](int r) -> const T* { return a.hn + (size_t)ids[base + min(r, rows - 1)] * a.H; });
   t.run(smem, a.H / Tile::kBK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
