@@ -87,6 +87,11 @@ struct EpiRouterIn {
   const T* s_in;  // NULL: block-0 semantics
   T* u;
   int R;
+  // Where the state loads read: rss and s_in with a carried state, else the bias with a
+  // row stride of 0 (read, never used). Set by the launcher, so the loads need no select.
+  const T* rss_ld = nullptr;
+  const T* st_ld = nullptr;
+  int st_stride = 0;
   using Row = EpiNone;
   struct Col {
     float bb[4], sc[4];
@@ -95,20 +100,23 @@ struct EpiRouterIn {
     float st[4];
   };
   __device__ __forceinline__ void load_row(int, Row&) const {}
+  // the state loads are unconditional, so no branch separates them
   __device__ __forceinline__ void load_col(int n, Col& c) const {
     load4(b + n, c.bb);
-    if (s_in) load4(rss + n, c.sc);
+    load4(rss_ld + n, c.sc);
   }
   __device__ __forceinline__ void load_elem(int m, int n, const Row&, Elem& e) const {
-    if (s_in) load4(s_in + (size_t)m * R + n, e.st);
+    load4(st_ld + (size_t)m * st_stride + n, e.st);
   }
   __device__ __forceinline__ void apply(int m, int n, const float* v, const Row&, const Col& c, const Elem& e) const {
     float o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = Act<T>::rnd(v[q] + c.bb[q]);
-    if (s_in)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = Act<T>::rnd(o[q] + Act<T>::rnd(c.sc[q] * e.st[q]));
+    for (int q = 0; q < 4; ++q) {
+      o[q] = Act<T>::rnd(v[q] + c.bb[q]);
+      // computed either way and selected (a branch would pull the state loads into it)
+      const float with_state = Act<T>::rnd(o[q] + Act<T>::rnd(c.sc[q] * e.st[q]));
+      o[q] = s_in ? with_state : o[q];
+    }
     store4(u + (size_t)m * R + n, o);
   }
   __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
@@ -351,7 +359,11 @@ hipError_t launch_gemm_merge(const T* O, const T* Wo, int M, int H, int K, const
 template <typename T>
 hipError_t launch_gemm_router_in(const T* hn, const T* Wd, int M, int R, int H, const T* b, const T* rss,
                                  const T* s_in, T* u, float* part, size_t part_bytes, hipStream_t s) {
-  return launch_any(hn, H, Wd, H, M, R, H, EpiRouterIn<T>{b, rss, s_in, u, R}, part, part_bytes, s);
+  EpiRouterIn<T> epi{b, rss, s_in, u, R};
+  epi.rss_ld = s_in ? rss : b;
+  epi.st_ld = s_in ? s_in : b;
+  epi.st_stride = s_in ? R : 0;
+  return launch_any(hn, H, Wd, H, M, R, H, epi, part, part_bytes, s);
 }
 
 #define ZAYA_INST(T)                                                                                                 \
