@@ -545,10 +545,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   // stage the token rows (rows past the tile repeat its last row; never stored)
   {
     const int cpr = K / 8;  // 16-byte chunks per row
-    for (int c0 = threadIdx.x; c0 < kF8Tok * cpr; c0 += 256 * 4) {
-      u32x4 v[4];
+    for (int c0 = threadIdx.x; c0 < kF8Tok * cpr; c0 += 256 * 8) {  // eight rows' loads in flight
+      u32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int ch = c0 + u * 256;
         if (ch < kF8Tok * cpr) {
           const int r = ch / cpr, cc = ch % cpr;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int ch = c0 + u * 256;
         if (ch < kF8Tok * cpr) *reinterpret_cast<u32x4*>(xs + (ch / cpr) * pitch + (ch % cpr) * 16) = v[u];
       }
