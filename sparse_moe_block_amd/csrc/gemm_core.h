@@ -26,6 +26,7 @@ template <typename T, int BM, int BN, int WM, int WN, bool STREAM_B = false>
 struct GemmTile {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
+  static constexpr int kBM = BM, kBN = BN, kWM = WM, kWN = WN;
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kRowBytes = 128;                    // one K slice of a row
   static constexpr int kBK = kRowBytes / (int)sizeof(T);   // K elements per slice

@@ -217,6 +217,8 @@ struct MoeArgs {
   int32_t* ids_out = nullptr;
   // W_gu / W_dn in the packed layout of launch_pack_experts (act-dtype experts only)
   int packed = 0;
+  // workgroups resident on the device at once (set by the launchers; see moe_item)
+  int slots = 0;
 };
 // Packed expert weights: rows in groups of kPackRows, each group stored slice after
 // slice (kPackSliceBytes of every row of the group, row after row), groups of an

@@ -18,6 +18,8 @@
 // Gate and up weight rows are interleaved in 16-row blocks inside each weight tile,
 // so every lane holds a gate and an up accumulator for the same outputs and SwiGLU
 // happens in registers.
+#include <atomic>
+
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -253,8 +255,16 @@ constexpr bool kStreamFewRows = true;
 // neighbouring items of one expert: they share its token rows and, across row tiles,
 // each weight tile through that XCD's L2. Returns false for workgroups past the real
 // items (the grid is sized for the worst case on the host).
-__device__ __forceinline__ bool moe_item(const int32_t* __restrict__ off, int E, int BM, int ntn, int& e_out,
-                                         int& r0_out, int& n_out, int& nt_out) {
+//
+// Tail split. The items run in rounds of `slots` (the workgroups resident on the whole
+// chip at once); a last round of a few items would leave most of the chip idle for an
+// item's whole duration (560 down items on 512 slots: a second round of 48). When
+// split > 1 and the items past the last full round, split into `split` column parts
+// each, fit one round, those parts are items of their own: every XCD runs its share of
+// full items (in contiguous runs, as above), then its share of the parts. part_out is
+// the column part (0 .. split - 1) of such an item, or -1 for a whole item.
+__device__ __forceinline__ bool moe_item(const int32_t* __restrict__ off, int E, int BM, int ntn, int slots, int split,
+                                         int& e_out, int& r0_out, int& n_out, int& nt_out, int& part_out) {
   // Every wave finds the item on its own: lane e < E reads offsets e and e + 1 (one
   // memory round trip; the offsets may live in LDS or in global memory), the row-tile
   // counts are scanned across lanes, and the expert holding the item is the first lane
@@ -271,11 +281,27 @@ __device__ __forceinline__ bool moe_item(const int32_t* __restrict__ off, int E,
   }
   const int tiles = __shfl(incl, 63, 64);
   const int n_real = tiles * ntn;
-  const int per = (n_real + 7) / 8;
-  const int k = (int)blockIdx.x / 8;
-  if (k >= per) return false;
-  int item = (int)(blockIdx.x % 8) * per + k;
-  if (item >= n_real) return false;
+  const int x = (int)blockIdx.x % 8, k = (int)blockIdx.x / 8;
+  const int nfull = slots > 0 ? n_real / slots * slots : n_real;  // slots: a multiple of 8
+  const int nsub = (n_real - nfull) * split;
+  int item;
+  part_out = -1;
+  if (split > 1 && nsub > 0 && nsub <= slots) {
+    const int fx = nfull / 8, spx = (nsub + 7) / 8;
+    if (k < fx) {
+      item = x * fx + k;
+    } else {
+      const int sub = x * spx + (k - fx);
+      if (k - fx >= spx || sub >= nsub) return false;
+      item = nfull + sub / split;
+      part_out = sub % split;
+    }
+  } else {
+    const int per = (n_real + 7) / 8;
+    if (k >= per) return false;
+    item = x * per + k;
+    if (item >= n_real) return false;
+  }
   const unsigned long long past = __ballot(lane < E && incl * ntn > item);
   const int e = __ffsll((long long)past) - 1;
   const int mt_e = __shfl(mt, e, 64);
@@ -287,45 +313,32 @@ __device__ __forceinline__ bool moe_item(const int32_t* __restrict__ off, int E,
   return true;
 }
 
-// Grid for a grouped GEMM: an upper bound on the items, rounded to the 8 XCDs.
-static inline int moe_grid(int ntok, int E, int BM, int ntn) {
+// Grid for a grouped GEMM: an upper bound on the items, rounded to the 8 XCDs, plus
+// the split tail's parts (at most one round of `slots`).
+static inline int moe_grid(int ntok, int E, int BM, int ntn, int slots = 0) {
   const int nmax = ((ntok + BM - 1) / BM + E) * ntn;
-  return 8 * ((nmax + 7) / 8);
+  return 8 * ((nmax + 7) / 8) + 8 * ((slots + 7) / 8);
 }
 
-// BN weight rows per item = BN/2 activation columns, gate and up in alternating 16-row
-// blocks.
-template <typename T, int BM, int WM, int WN, int BN = 128>
-__global__ __launch_bounds__(WM* WN * 64)
-__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
-  constexpr int CN = BN / 2;  // activation columns per item
-  using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
+// One gate/up item: Tile::kBN weight rows = kBN / 2 activation columns starting at c0,
+// gate and up in alternating 16-row blocks; q0 is the item's first row within its
+// 128-row group (the group's rows are in that order, packed or not).
+template <typename T, class Tile>
+__device__ __forceinline__ void gateup_item(const MoeArgs<T>& a, const int32_t* __restrict__ ids, char* smem, int e,
+                                            int base, int rows, int grp, int q0) {
   static_assert(Tile::kTN % 2 == 0, "each wave needs gate/up pairs");
   static_assert(Tile::kRowBytes == kPackSliceBytes, "packed slices are the tile's K slices");
-  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
-  __shared__ SmallBuckets sb;
-  const int32_t* off = a.offsets;
-  const int32_t* ids = a.ids;
-  if (a.cls) {  // few tokens: the buckets are formed here
-    small_buckets(a.cls, a.ntok, a.E, sb, a.offsets_out, a.ids_out);
-    off = sb.off;
-    ids = sb.ids;
-  }
-  int e, r0, n_e, j;  // j: activation columns [CN j, CN j + CN)
-  if (!moe_item(off, a.E, BM, a.I / CN, e, r0, n_e, j)) return;
-  const int base = off[e] + r0;
-  const int rows = min(BM, n_e - r0);
+  const int c0 = grp * (kPackRows / 2) + q0 / 2;  // activation columns [c0, c0 + kBN / 2)
   Tile t;
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
-  if (a.packed) {  // the item's 128 rows are packed group j, in the same row order
-    static_assert(BN == kPackRows, "a gate/up item is one packed row group");
-    const T* Wgrp = Wg + (size_t)j * kPackRows * a.H;
-    t.set_b([&](int r) -> const T* { return Wgrp + (size_t)r * Tile::kBK; });
+  if (a.packed) {  // the item's rows are rows q0 .. of packed group grp
+    const T* Wgrp = Wg + (size_t)grp * kPackRows * a.H;
+    t.set_b([&](int r) -> const T* { return Wgrp + (size_t)(q0 + r) * Tile::kBK; });
     t.bstride = (size_t)kPackRows * Tile::kRowBytes;
   } else {
     t.set_b([&](int r) -> const T* {
       const int blk = r >> 4, w16 = r & 15;
-      const int row = ((blk & 1) ? a.I : 0) + CN * j + (blk >> 1) * 16 + w16;
+      const int row = ((blk & 1) ? a.I : 0) + c0 + (blk >> 1) * 16 + w16;
       return Wg + (size_t)row * a.H;
     });
   }
@@ -333,7 +346,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   t.run(smem, a.H / Tile::kBK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / Tile::kWN, wn = wave % Tile::kWN;
 #pragma unroll
   for (int i = 0; i < Tile::kTM; ++i) {
     const int m = wm * Tile::kTM * 16 + i * 16 + (lane & 15);
@@ -341,7 +354,7 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
     T* nrow = a.neurons + (size_t)(base + m) * a.I;
 #pragma unroll
     for (int pp = 0; pp < Tile::kTN / 2; ++pp) {
-      const int col = CN * j + (wn * (Tile::kTN / 2) + pp) * 16 + (lane >> 4) * 4;
+      const int col = c0 + (wn * (Tile::kTN / 2) + pp) * 16 + (lane >> 4) * 4;
       float v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -353,6 +366,35 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
       store4(nrow + col, v);
     }
   }
+}
+
+// BN = 128 weight rows per item (one 128-row group: 64 activation columns); with
+// SPLIT > 1 the tail items of moe_item run as SPLIT parts of BN / SPLIT rows (waves
+// stacked along the rows when a part is too narrow to give every wave gate/up pairs).
+template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
+  static_assert(BN == kPackRows, "a gate/up item is one 128-row group");
+  using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
+  constexpr bool kNarrow = BN / SPLIT < WN * 32;
+  using Part = GemmTile<T, BM, BN / SPLIT, kNarrow ? WM * WN : WM, kNarrow ? 1 : WN, (BM <= 16 && kStreamFewRows)>;
+  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  __shared__ SmallBuckets sb;
+  const int32_t* off = a.offsets;
+  const int32_t* ids = a.ids;
+  if (a.cls) {  // few tokens: the buckets are formed here
+    small_buckets(a.cls, a.ntok, a.E, sb, a.offsets_out, a.ids_out);
+    off = sb.off;
+    ids = sb.ids;
+  }
+  int e, r0, n_e, j, part;  // j: the 128-row group (activation columns [64 j, 64 j + 64))
+  if (!moe_item(off, a.E, BM, a.I / (BN / 2), SPLIT > 1 ? a.slots : 0, SPLIT, e, r0, n_e, j, part)) return;
+  const int base = off[e] + r0;
+  const int rows = min(BM, n_e - r0);
+  if (SPLIT > 1 && part >= 0)
+    gateup_item<T, Part>(a, ids, smem, e, base, rows, j, part * (BN / SPLIT));
+  else
+    gateup_item<T, Tile>(a, ids, smem, e, base, rows, j, 0);
 }
 
 // Down-projection epilogue: y = rnd(sum), routed = rnd(w * y), mlp = rnd(rnd(routed + hsb)
@@ -403,21 +445,14 @@ struct EpiDownMerge {
   }
 };
 
-template <typename T, int BM, int WM, int WN, int BN = 128>
-__global__ __launch_bounds__(WM* WN * 64)
-__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
-  using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
-  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
-  int e, r0, n_e, c;
-  if (!moe_item(a.offsets, a.E, BM, a.H / BN, e, r0, n_e, c)) return;
-  const int n0 = c * BN;
-  const int base = a.offsets[e] + r0;
-  const int rows = min(BM, n_e - r0);
+// One down item: output columns n0 .. n0 + Tile::kBN of the item's token rows.
+template <typename T, class Tile>
+__device__ __forceinline__ void down_item(const MoeArgs<T>& a, char* smem, int e, int base, int rows, int n0) {
   Tile t;
   t.set_a([&](int r) -> const T* { return a.neurons + (size_t)(base + min(r, rows - 1)) * a.I; });
   const T* Wd = a.W_dn + (size_t)e * a.H * a.I;
-  if (a.packed) {  // rows n0 .. n0 + BN lie in packed group n0 / 128
-    static_assert(kPackRows % BN == 0, "a down item lies in one packed row group");
+  if (a.packed) {  // rows n0 .. n0 + kBN lie in packed group n0 / 128
+    static_assert(kPackRows % Tile::kBN == 0, "a down item lies in one packed row group");
     const T* Wgrp = Wd + (size_t)(n0 / kPackRows) * kPackRows * a.I;
     const int q0 = n0 % kPackRows;
     t.set_b([&](int r) -> const T* { return Wgrp + (size_t)(q0 + r) * Tile::kBK; });
@@ -429,16 +464,56 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   t.epilogue_loaded(EpiDownMerge<T>{a, base, n0}, rows);
 }
 
-template <typename T, int BM, int WM, int WN, int BN = 128>
-static hipError_t launch_gateup_cfg(const MoeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN, BN>), dim3(moe_grid(a.ntok, a.E, BM, a.I / (BN / 2))),
+// BN output columns per item; with SPLIT > 1 the tail items of moe_item run as SPLIT
+// parts of BN / SPLIT columns.
+template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_down_kernel(MoeArgs<T> a) {
+  using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
+  constexpr bool kNarrow = BN / SPLIT < WN * 16;  // then the part's waves stack along the rows
+  using Part = GemmTile<T, BM, BN / SPLIT, kNarrow ? WM * WN : WM, kNarrow ? 1 : WN, (BM <= 16 && kStreamFewRows)>;
+  __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
+  int e, r0, n_e, c, part;
+  if (!moe_item(a.offsets, a.E, BM, a.H / BN, SPLIT > 1 ? a.slots : 0, SPLIT, e, r0, n_e, c, part)) return;
+  const int base = a.offsets[e] + r0;
+  const int rows = min(BM, n_e - r0);
+  if (SPLIT > 1 && part >= 0)
+    down_item<T, Part>(a, smem, e, base, rows, c * BN + part * (BN / SPLIT));
+  else
+    down_item<T, Tile>(a, smem, e, base, rows, c * BN);
+}
+
+// Workgroups of the 128 x 128 expert tiles resident on the current device at once (two
+// per CU), a multiple of 8; 0 if the device cannot be queried.
+static int moe_slots() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];  // per device: 0 = not yet asked, else slots + 1
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c - 1;
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int slots = (2 * cus) / 8 * 8;
+  if (dev >= 0 && dev < kMaxDev) cache[dev].store(slots + 1, std::memory_order_relaxed);
+  return slots;
+}
+
+template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
+static hipError_t launch_gateup_cfg(const MoeArgs<T>& a0, hipStream_t s) {
+  MoeArgs<T> a = a0;
+  a.slots = SPLIT > 1 ? moe_slots() : 0;
+  hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN, BN, SPLIT>), dim3(moe_grid(a.ntok, a.E, BM, a.I / (BN / 2), a.slots)),
                      dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int BM, int WM, int WN, int BN = 128>
-static hipError_t launch_down_cfg(const MoeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN, BN>), dim3(moe_grid(a.ntok, a.E, BM, a.H / BN)),
+template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
+static hipError_t launch_down_cfg(const MoeArgs<T>& a0, hipStream_t s) {
+  MoeArgs<T> a = a0;
+  a.slots = SPLIT > 1 ? moe_slots() : 0;
+  hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN, BN, SPLIT>), dim3(moe_grid(a.ntok, a.E, BM, a.H / BN, a.slots)),
                      dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -450,14 +525,14 @@ template <typename T>
 hipError_t launch_moe_gateup(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
   if (a.ntok <= 32 * a.E) return launch_gateup_cfg<T, 16, 1, 4>(a, s);
-  return launch_gateup_cfg<T, 128, 2, 2>(a, s);
+  return launch_gateup_cfg<T, 128, 2, 2, 128, 2>(a, s);
 }
 
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs<T>& a, hipStream_t s) {
   if (a.ntok <= 0) return hipSuccess;
   if (a.ntok <= 32 * a.E) return launch_down_cfg<T, 16, 1, 4, 64>(a, s);
-  return launch_down_cfg<T, 128, 2, 2>(a, s);
+  return launch_down_cfg<T, 128, 2, 2, 128, 4>(a, s);
 }
 
 // ----------------------------------------------------------------------------- FP8 experts
@@ -510,7 +585,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     ids = sb.ids;
   }
   int e, r0, n_e, j;
-  if (!moe_item(off, a.E, kF8Tok, ntn, e, r0, n_e, j)) return;
+  int part;
+  if (!moe_item(off, a.E, kF8Tok, ntn, 0, 1, e, r0, n_e, j, part)) return;
   const int base = off[e] + r0;
   const int rows = min(kF8Tok, n_e - r0);
   const int pitch = K * 2 + 16;
