@@ -455,51 +455,65 @@ __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a
 //                8 (r / 4) + 4 (l / 32) + r % 4, r < 16, of the block;
 //   O^T = V^T P^T in 32-dim x 32-query blocks over 16-key steps: the B operand of step
 //                ks is eight of the lane's score registers as they are (registers
-//                8 (ks % 2) .. +8 of key block ks / 2), and the V^T rows are read in the
-//                same key order (4-key units 4 ks + l / 32 and 4 ks + 2 + l / 32).
-// Each K/V tile in LDS serves 2 G waves. K tiles go from global memory straight into
-// LDS (global_load_lds, the swizzle applied on the global side); V goes through registers
-// and is transposed as it is written. Two LDS tile buffers, declared as two arrays so the
-// compiler's wait tracking sees that the direct loads into one cannot alias reads of the
-// other (one array made it wait for the next tile before every read of the current one:
-// 74.6 vs 72.0 us). The loop is unrolled by two, so every fragment read is a per-lane
-// offset (computed once) plus an immediate.
+//                8 (ks % 2) .. +8 of key block ks / 2: keys 16 ks + 4 (l / 32) + 0..3 and
+//                16 ks + 8 + 4 (l / 32) + 0..3), and the A operand holds the V values of
+//                the same keys for dim l % 32 of the block.
+// K and V tiles go from global memory straight into LDS (global_load_lds, row-major
+// [key][dim], a 16-byte-chunk swizzle applied on the global side) through a ring of LDS
+// slots declared as separate arrays (so the compiler's wait tracking sees that the loads
+// into one slot cannot alias reads of another): three slots, two tiles ahead of the
+// products, with 4 heads a group (one workgroup per CU); two slots, one tile ahead,
+// otherwise (two workgroups per CU fit only then). The V^T operands come from the row-major V tile through the LDS transpose
+// read (ds_read_b64_tr_b16): within each 16-lane group, lane a + 4 k addresses 4 dims
+// of key row k and lane 4 a + c receives dim c of that chunk for the 4 keys. Each wave
+// waits only for the tile the next step reads (the newest tile's loads stay in flight)
+// and the workgroup then meets at a bare barrier. The loop is unrolled by three, so every
+// fragment read is a per-lane offset (computed once) plus an immediate.
 namespace pf64 {
 constexpr int kQW = 64;                  // queries per workgroup (per head)
 constexpr int kD = 128;
-constexpr int kKRow = kD * 2;            // bytes per K row (bf16)
-constexpr int kVRow = 64 * 2;            // bytes per V^T row (64 keys)
-constexpr int kKBytes = 64 * kKRow;
-constexpr int kBuf = kKBytes + kD * kVRow;
+constexpr int kRow = kD * 2;             // bytes per K or V row (bf16)
+constexpr int kTileBytes = 64 * kRow;    // one 64-key K or V tile
+constexpr int kBuf = 2 * kTileBytes;     // a slot: K tile, then V tile
 // Measured on gfx950 for these fragment reads (32 key rows of one 16-byte chunk per
 // half wave): chunk c of key k stored at c ^ (k % 16) reads conflict-free (118 TB/s);
 // the swizzle of the 16x16 kernel drops to 69 TB/s here.
-__device__ __forceinline__ int koff(int key, int chunk) { return key * kKRow + ((chunk ^ (key & 15)) << 4); }
-// V^T: 8-byte unit u (4 keys) of dim row d at u ^ vswz(d), the mask of the kernel above:
-// no bank conflicts for these 32-row fragment reads nor for the transposing writes of
-// 4-key x 8-dim tasks (measured with the LDS conflict counter; (d / 2) % 16 reads as
-// fast but its writes conflict). For d = 32 db + r (r < 32) it equals vswz(r) ^ 2 db,
-// so dim block db's fragment sits db * 32 rows after block 0's, at unit u ^ 2 db.
-__device__ __forceinline__ int vswz(int d) { return (((d >> 1) & 7) << 1) ^ ((d >> 4) & 7); }
-__device__ __forceinline__ int voff(int d, int unit) { return d * kVRow + ((unit ^ vswz(d)) << 3); }
+__device__ __forceinline__ int koff(int key, int chunk) { return key * kRow + ((chunk ^ (key & 15)) << 4); }
+// V: chunk c of key k stored at c ^ vsw(k). A transpose read covers 8 consecutive keys
+// (a multiple of 8 onwards) x 32 bytes of one 64-byte dim block per 16-lane group, 512
+// bytes per wave: with 128 four-byte banks a key row spans half of them (even and odd
+// keys on opposite halves), and vsw puts the 64-byte blocks of the four keys of each
+// half in four different places.
+__device__ __forceinline__ int vsw(int key) { return ((key >> 1) & 3) << 2; }
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
+__device__ __forceinline__ uint2 read_tr(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) const char*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+// s_waitcnt immediate that waits until at most n vector memory operations are pending
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 }  // namespace pf64
 
 template <int G>
 __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill64_kernel(
     AttnArgs<bf16_t> a, float* __restrict__ part, int NC) {
   using namespace pf64;
-  constexpr int NT = 128 * G;
-  constexpr int VD = 8;                     // dims per V task (4 keys x 8 dims): 256 tasks
-  constexpr int VT = NT >= 256 ? 1 : 256 / NT;  // V tasks per thread (threads past 256 have none)
-  constexpr int VW = VD / 4;                // 8-byte words per key row of a task
-  const bool v_task = NT <= 256 || threadIdx.x < 256;  // whole waves
+  constexpr int NW = 2 * G;                // waves
+  constexpr int NSLOT = G == 4 ? 3 : 2;    // ring slots; tiles in flight ahead: NSLOT - 1
+  constexpr int kLoads = 8 / G;            // 16-byte load instructions per thread per K (or V) tile
+  constexpr int kTileLoads = 2 * kLoads;   // per thread per tile (K and V)
+  constexpr int kPendOk = (NSLOT - 2) * kTileLoads;  // loads that may stay in flight at a step's end
+  static_assert(NW * kLoads * 4 == 64, "one tile: 64 rows of 4 per instruction");
   __shared__ __attribute__((aligned(1024))) char lds0[kBuf];
   __shared__ __attribute__((aligned(1024))) char lds1[kBuf];
+  __shared__ __attribute__((aligned(1024))) char lds2[NSLOT == 3 ? kBuf : 16];
 
   const int nqb = (a.S + kQW - 1) / kQW;
   const int c = blockIdx.x % NC;
@@ -523,7 +537,29 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bf16_t* Vb = a.V + ((size_t)b * a.nkv + g) * a.cap * kD;
   const float sscale = kLog2e / sqrtf((float)kD);
 
-  // this lane's query (zero past S): dims 16 ds + 8 hl .. + 8
+  // Tile loads: instruction j of a wave fills key rows kr0 .. kr0 + 3 (1 KiB, 16 bytes a
+  // lane, in LDS order); the lane at position p of its row fetches the chunk stored
+  // there. Key rows past kvalid - 1 re-read that row: those keys come after every query
+  // of the call, so their scores are masked and their probabilities are exactly 0; tiles
+  // past the unit's range re-read valid rows into a slot nothing reads.
+  auto issue_tile = [&](char* buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int kr0 = (wave * kLoads + j) * 4;
+      const int key = kr0 + (lane >> 4);
+      const bf16_t* src = Kb + (size_t)min(k0 + key, kvalid - 1) * kD + (((lane & 15) ^ (key & 15)) << 3);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + kr0 * kRow), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int kr0 = (wave * kLoads + j) * 4;
+      const int key = kr0 + (lane >> 4);
+      const bf16_t* src = Vb + (size_t)min(k0 + key, kvalid - 1) * kD + (((lane & 15) ^ vsw(key)) << 3);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + kTileBytes + kr0 * kRow), 16,
+                                       0, 0);
+    }
+  };
+  // this lane's query (zero past S): dims 16 ds + 8 hl .. + 8; then the first tiles
   uint4 qf[8];
   {
     const int t = q0 + row;
@@ -534,71 +570,24 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
       qf[ds] = t < S ? v : make_uint4(0, 0, 0, 0);
     }
   }
-  // fragment offsets within a buffer: K for step ds (key block 0; block 1 is 32 rows on),
-  // V^T of dim block 0 for unit 4 k + 2 hi + hl (block db: 32 db rows on, at the unit
-  // XOR 2 db, i.e. k ^ db / 2 and hi ^ db % 2)
-  int ko[8], vo[8];
+  issue_tile(lds0, kt0 * 64);
+  if constexpr (NSLOT == 3) issue_tile(lds1, (kt0 + 1) * 64);
+  // fragment offsets within a slot: K for step ds (key block 0; block 1 is 32 rows on);
+  // V for dim block db (PV step ks and its second four keys: immediates on top). A lane
+  // of 16-lane group gi = lane / 16 at position i reads key row 4 hl + i / 4 (+ 16 ks,
+  // + 8), dims 32 db + 16 (gi % 2) + 4 (i % 4) .. + 3.
+  int ko[8], vo[4];
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) ko[ds] = koff(l32, 2 * ds + hl);
+  {
+    const int i = lane & 15, gi = lane >> 4;
+    const int vkey = 4 * hl + (i >> 2);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) vo[2 * k + hi] = kKBytes + voff(l32, 4 * k + 2 * hi + hl);
-
-  // Tile loads. Key rows past kvalid - 1 re-read that row: those keys come after every
-  // query of the call, so their scores are masked and their probabilities are exactly 0.
-  auto issue_k = [&](char* buf, int k0) {
-#pragma unroll
-    for (int j = 0; j < 8 / G; ++j) {
-      const int kr0 = (wave * (8 / G) + j) * 4;
-      const int key = kr0 + (lane >> 4);
-      const int chunk = (lane & 15) ^ (key & 15);
-      const bf16_t* src = Kb + (size_t)min(k0 + key, kvalid - 1) * kD + chunk * 8;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + kr0 * kKRow), 16, 0, 0);
+    for (int db = 0; db < 4; ++db) {
+      const int byte = 64 * db + 32 * (gi & 1) + 8 * (i & 3);
+      vo[db] = kTileBytes + vkey * kRow + ((((byte >> 4) ^ vsw(vkey))) << 4) + (byte & 15);
     }
-  };
-  uint2 vr[VT][4][VW];  // task i, key kk: VD dims as 8-byte words
-  auto load_v = [&](int k0) {
-    if (!v_task) return;
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-      const int task = (int)threadIdx.x + i * NT;
-      const int q4 = task / (kD / VD), dq = task % (kD / VD);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16_t* src = Vb + (size_t)min(k0 + 4 * q4 + kk, kvalid - 1) * kD + dq * VD;
-        if constexpr (VW == 2) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src);
-          vr[i][kk][0] = make_uint2(v.x, v.y);
-          vr[i][kk][1] = make_uint2(v.z, v.w);
-        } else {
-          vr[i][kk][0] = *reinterpret_cast<const uint2*>(src);
-        }
-      }
-    }
-  };
-  // V^T row d = VD dq + j, unit q4: keys 4 q4 .. +3 of dim d, packed two keys a word
-  auto store_v = [&](char* buf) {
-    if (!v_task) return;
-    char* vt = buf + kKBytes;
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-      const int task = (int)threadIdx.x + i * NT;
-      const int q4 = task / (kD / VD), dq = task % (kD / VD);
-#pragma unroll
-      for (int j = 0; j < VD; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        auto word = [&](int kk) -> uint32_t {
-          const uint2 q = vr[i][kk][j >> 2];
-          return ((j >> 1) & 1) ? q.y : q.x;
-        };
-        uint2 w;
-        w.x = __builtin_amdgcn_perm(word(1), word(0), sel);
-        w.y = __builtin_amdgcn_perm(word(3), word(2), sel);
-        *reinterpret_cast<uint2*>(vt + voff(dq * VD + j, q4)) = w;
-      }
-    }
-  };
+  }
 
   f32x16 o[4];
 #pragma unroll
@@ -607,16 +596,13 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // one key tile j in LDS buffer B; with `more`, tile j + 1 loads into the other buffer
-  auto step = [&](auto buf_tag, int j) {
-    constexpr int B = decltype(buf_tag)::value;
-    const char* buf = B == 0 ? lds0 : lds1;
-    char* other = B == 0 ? lds1 : lds0;
-    const bool more = j + 1 < kt1;
-    if (more) {
-      issue_k(other, (j + 1) * 64);
-      load_v((j + 1) * 64);
-    }
+  // One key tile j in ring slot B; tile j + NSLOT - 1 loads into the slot before it.
+  auto step = [&](auto slot_tag, int j) {
+    constexpr int B = decltype(slot_tag)::value;
+    constexpr int BA = (B + NSLOT - 1) % NSLOT;
+    const char* buf = B == 0 ? lds0 : (B == 1 ? lds1 : lds2);
+    char* ahead = BA == 0 ? lds0 : (BA == 1 ? lds1 : lds2);
+    issue_tile(ahead, (j + NSLOT - 1) * 64);
     const int k0 = j * 64;
     // S^T = K Q^T
     f32x16 s[2];
@@ -628,7 +614,7 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ds = 0; ds < 8; ++ds)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(buf + ko[ds] + kb * 32 * kKRow);
+        const uint4 kf = *reinterpret_cast<const uint4*>(buf + ko[ds] + kb * 32 * kRow);
         s[kb] = mma(kf, qf[ds], s[kb]);
       }
     // mask where the tile cuts the causal / window band; running max; rescale
@@ -683,30 +669,39 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(buf + vo[2 * (ks ^ (db >> 1)) + (db & 1)] + db * 32 * kVRow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(buf + vo[2 * (ks ^ (db >> 1)) + (1 ^ (db & 1))] + db * 32 * kVRow);
+        const uint2 lo = read_tr(buf + vo[db] + 16 * ks * kRow);
+        const uint2 hi = read_tr(buf + vo[db] + (16 * ks + 8) * kRow);
         o[db] = mma(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[ks], o[db]);
       }
-    if (more) {
-      asm volatile("" ::: "memory");  // keep the stores (and their wait for the loads) here
-      store_v(other);
-    }
-    // this wave's direct K loads into the other buffer have landed before the barrier
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-    __syncthreads();
+    // tile j + 1 has landed for this wave (with three slots tile j + 2's loads, the
+    // youngest, stay in flight); after the barrier every wave's part of it has
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPendOk));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
-  using Buf0 = std::integral_constant<int, 0>;
-  using Buf1 = std::integral_constant<int, 1>;
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Slot2 = std::integral_constant<int, 2>;
 
-  issue_k(lds0, kt0 * 64);
-  load_v(kt0 * 64);
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-  store_v(lds0);
-  __syncthreads();
-  for (int j = kt0; j < kt1; j += 2) {
-    step(Buf0{}, j);
-    if (j + 1 < kt1) step(Buf1{}, j + 1);
+  // the queries and tile kt0 have landed (with three slots tile kt0 + 1 may be in flight)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPendOk));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  // whole rounds of the ring first (no branch inside, so the compiler's wait tracking
+  // sees the same loads in flight on every path back to the loop's head), then the rest
+  int j = kt0;
+  for (; j + NSLOT <= kt1; j += NSLOT) {
+    step(Slot0{}, j);
+    step(Slot1{}, j + 1);
+    if constexpr (NSLOT == 3) step(Slot2{}, j + 2);
   }
+  if (j < kt1) step(Slot0{}, j);
+  if constexpr (NSLOT == 3)
+    if (j + 1 < kt1) step(Slot1{}, j + 1);
+  // no load may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // lane holds O^T[d = 32 db + 8 (r / 4) + 4 hl + r % 4][its query]; the row sum is
   // split over lanes l32 and l32 + 32
