@@ -515,10 +515,15 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(1024))) char lds1[kBuf];
   __shared__ __attribute__((aligned(1024))) char lds2[NSLOT == 3 ? kBuf : 16];
 
+  // units heaviest first over the whole grid: (query tile from the last, chunk), then
+  // KV group and sequence fastest, so the longest units of every group and sequence
+  // start in the first round
   const int nqb = (a.S + kQW - 1) / kQW;
-  const int c = blockIdx.x % NC;
-  const int qblk = nqb - 1 - (int)(blockIdx.x / NC);
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int ngb = a.nkv * a.B;
+  const int gb = (int)blockIdx.x % ngb, r = (int)blockIdx.x / ngb;
+  const int c = r % NC;
+  const int qblk = nqb - 1 - r / NC;
+  const int g = gb % a.nkv, b = gb / a.nkv;
   const int S = a.S, L0 = cached_len(a.cache_len, b), W = a.window;
   const QTile qt = qtile<kQW>(qblk, S, L0, W, NC);
   if (c >= qt.nc) return;
@@ -996,7 +1001,7 @@ template <typename T, int D, int G>
 static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && D == 128 && G <= 4) {
     const int nqb = (a.S + pf64::kQW - 1) / pf64::kQW;
-    hipLaunchKernelGGL((attn_prefill64_kernel<G>), dim3(nqb * NC, a.nkv, a.B), dim3(128 * G), 0, s, a, part, NC);
+    hipLaunchKernelGGL((attn_prefill64_kernel<G>), dim3(nqb * NC * a.nkv * a.B), dim3(128 * G), 0, s, a, part, NC);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || NC == 1) return e;
     using CS = CombineShape<D, G>;

@@ -146,7 +146,7 @@ struct EpiAt {
   }
 };
 
-template <typename T, int BM, int BN, int WM, int WN, class Epi>
+template <typename T, int BM, int BN, int WM, int WN, class Epi, int NST>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void gemm_nt_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
                                                                int ldb, int M, int N, int K, Epi epi) {
@@ -158,15 +158,15 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
   Tile t;
   t.set_a([&](int r) -> const T* { return A + (size_t)min(m0 + r, M - 1) * lda; });
   t.set_b([&](int r) -> const T* { return B + (size_t)min(n0 + r, N - 1) * ldb; });
-  t.run(smem, K / Tile::kBK);
+  t.template run<NST>(smem, K / Tile::kBK);
   t.epilogue_loaded(EpiAt<Epi>{epi, m0, n0}, min(BM, M - m0), min(BN, N - n0));
 }
 
-template <typename T, int BM, int BN, int WM, int WN, class Epi>
+template <typename T, int BM, int BN, int WM, int WN, class Epi, int NST = 3>
 static hipError_t launch_cfg(const T* A, int lda, const T* B, int ldb, int M, int N, int K, Epi epi, hipStream_t s) {
   const int g = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi>), dim3(g), dim3(WM * WN * 64), 0, s, A, lda, B, ldb, M,
-                     N, K, epi);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi, NST>), dim3(g), dim3(WM * WN * 64), 0, s, A, lda, B, ldb,
+                     M, N, K, epi);
   return hipGetLastError();
 }
 
@@ -259,10 +259,12 @@ static int splitk_parts(int ntiles, int K, int kBK, size_t elems, size_t part_by
 }
 
 // Tile choice. GEMMs with few rows (decode) split K into parts reduced by a second
-// pass (they stream weights). Otherwise the tile is picked by a cost model: a CU runs two 128-row tiles at once,
-// so the cost of a tile shape is (rounds of 512 tiles) x (tile area); 128x96 wins when
-// it fills the rounds that 128x128 leaves partly empty (N = 1536: 512 tiles instead of
-// 384). Small grids use 64x64 or 32x64 tiles.
+// pass (they stream weights). Otherwise the tile is picked by a cost model: a CU runs
+// two 4-wave workgroups (128x96, 128x128) or one 8-wave workgroup (128x192, 128x256) at
+// once, so a shape costs (rounds of resident workgroups) x (workgroups per CU) x (tile
+// area), the 8-wave shapes at 0.88 of that: they read and stage each A slice once for
+// twice the columns (measured on the q/k/v shape: 35.4 vs 40.2 us; o_proj: 27.4 vs
+// 29.4 us). Small grids use 64x64 or 32x64 tiles.
 template <typename T, class Epi>
 static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, int N, int K, Epi epi, float* part,
                              size_t part_bytes, hipStream_t s) {
@@ -282,11 +284,16 @@ static hipError_t launch_any(const T* A, int lda, const T* B, int ldb, int M, in
       return hipGetLastError();
     }
   }
-  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  const long t96 = (long)((M + 127) / 128) * ((N + 95) / 96);
+  const long mt = (M + 127) / 128;
+  const long t128 = mt * ((N + 127) / 128);
   if (t128 >= 240) {
-    const long c128 = (t128 + 511) / 512 * 128, c96 = (t96 + 511) / 512 * 96;
-    if (c96 < c128) return launch_cfg<T, 128, 96, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
+    const long t96 = mt * ((N + 95) / 96), t192 = mt * ((N + 191) / 192), t256 = mt * ((N + 255) / 256);
+    const double c96 = (double)((t96 + 511) / 512) * 2 * 96, c128 = (double)((t128 + 511) / 512) * 2 * 128;
+    const double c192 = (double)((t192 + 255) / 256) * 192 * 0.88, c256 = (double)((t256 + 255) / 256) * 256 * 0.88;
+    const double best = fmin(fmin(c96, c128), fmin(c192, c256));
+    if (best == c192) return launch_cfg<T, 128, 192, 2, 4, Epi, 4>(A, lda, B, ldb, M, N, K, epi, s);
+    if (best == c256) return launch_cfg<T, 128, 256, 2, 4, Epi, 3>(A, lda, B, ldb, M, N, K, epi, s);
+    if (best == c96) return launch_cfg<T, 128, 96, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
     return launch_cfg<T, 128, 128, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);
   }
   if (t64 >= 120) return launch_cfg<T, 64, 64, 2, 2>(A, lda, B, ldb, M, N, K, epi, s);

@@ -38,8 +38,8 @@ struct GemmTile {
   static constexpr int kBufBytes = (BM + BN) * kRowBytes;
   static constexpr int kLdsBytes = 2 * kBufBytes;
   // Waves per SIMD the kernel is compiled for (register budget 512 / waves): 2 for the
-  // 128x96 and 128x128 tiles (their LDS already allows only two workgroups per CU), 4
-  // for the smaller ones.
+  // tiles of 128x96 and up (their LDS already allows only two 4-wave or one 8-wave
+  // workgroup per CU), 4 for the smaller ones.
   static constexpr int kWavesPerEU = BM * BN >= 128 * 96 ? 2 : 4;
   static_assert(BM % (WM * 16) == 0 && BN % (WN * 16) == 0, "tile must split into 16x16 blocks");
   static_assert(kKSteps >= 1, "slice too short");
@@ -159,9 +159,9 @@ struct GemmTile {
 
   // Full K loop over nk slices. lds: kLdsBytes of shared memory.
   //
-  // Global loads run three slices ahead of the MFMAs: slice k+1 goes from its register
-  // stage to the idle LDS buffer right after slice k's products, and that stage is
-  // refilled at once with slice k+4. One barrier per slice. The three stages are named
+  // Global loads run NST (3 or 4) slices ahead of the MFMAs: slice k+1 goes from its
+  // register stage to the idle LDS buffer right after slice k's products, and that stage
+  // is refilled at once with slice k+NST+1. One barrier per slice. The stages are named
   // variables and the loop is unrolled by hand, so nothing is indexed at run time.
   //
   // The main loop has no data-dependent branches: past the end, the refill re-reads the
@@ -172,13 +172,20 @@ struct GemmTile {
     u32x4 a[kAChunks];
     u32x4 b[kBChunks];
   };
+  template <int NST>
   __device__ __forceinline__ void step(char* lds, int kt, int nk, Stage& st) {
     compute_slice(lds + (kt & 1) * kBufBytes);
     store_slice(lds + ((kt + 1) & 1) * kBufBytes, st.a, st.b);
-    load_slice(min(kt + 4, nk - 1), st.a, st.b);
+    load_slice(min(kt + NST + 1, nk - 1), st.a, st.b);
     __syncthreads();
   }
+  template <int NST = 3>
   __device__ __forceinline__ void run(char* lds, int nk) {
+    static_assert(NST == 3 || NST == 4, "three or four register stages");
+    if constexpr (NST == 4) {
+      run4(lds, nk);
+      return;
+    }
     zero_acc();
     Stage s0, s1, s2;
     // B rows first: their addresses never wait on a gather (A's rows may be token rows
@@ -194,12 +201,37 @@ struct GemmTile {
     __syncthreads();
     int k0 = 0;
     for (; k0 + 3 <= nk; k0 += 3) {
-      step(lds, k0, nk, s1);      // slice k0+1 is in s1
-      step(lds, k0 + 1, nk, s2);  // slice k0+2 is in s2
-      step(lds, k0 + 2, nk, s0);  // slice k0+3 is in s0
+      step<3>(lds, k0, nk, s1);      // slice k0+1 is in s1
+      step<3>(lds, k0 + 1, nk, s2);  // slice k0+2 is in s2
+      step<3>(lds, k0 + 2, nk, s0);  // slice k0+3 is in s0
     }
-    if (k0 < nk) step(lds, k0, nk, s1);
-    if (k0 + 1 < nk) step(lds, k0 + 1, nk, s2);
+    if (k0 < nk) step<3>(lds, k0, nk, s1);
+    if (k0 + 1 < nk) step<3>(lds, k0 + 1, nk, s2);
+  }
+  __device__ __forceinline__ void run4(char* lds, int nk) {
+    zero_acc();
+    Stage s0, s1, s2, s3;
+    load_b(0, s0.b);
+    load_b(min(1, nk - 1), s1.b);
+    load_b(min(2, nk - 1), s2.b);
+    load_b(min(3, nk - 1), s3.b);
+    load_a(0, s0.a);
+    load_a(min(1, nk - 1), s1.a);
+    load_a(min(2, nk - 1), s2.a);
+    load_a(min(3, nk - 1), s3.a);
+    store_slice(lds, s0.a, s0.b);
+    load_slice(min(4, nk - 1), s0.a, s0.b);
+    __syncthreads();
+    int k0 = 0;
+    for (; k0 + 4 <= nk; k0 += 4) {
+      step<4>(lds, k0, nk, s1);
+      step<4>(lds, k0 + 1, nk, s2);
+      step<4>(lds, k0 + 2, nk, s3);
+      step<4>(lds, k0 + 3, nk, s0);
+    }
+    if (k0 < nk) step<4>(lds, k0, nk, s1);
+    if (k0 + 1 < nk) step<4>(lds, k0 + 1, nk, s2);
+    if (k0 + 2 < nk) step<4>(lds, k0 + 2, nk, s3);
   }
 
   // Epilogue with loads: every global read the epilogue needs is issued before the first

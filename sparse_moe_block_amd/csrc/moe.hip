@@ -321,8 +321,9 @@ static inline int moe_grid(int ntok, int E, int BM, int ntn, int slots = 0) {
 }
 
 // One gate/up item: Tile::kBN weight rows = kBN / 2 activation columns starting at c0,
-// gate and up in alternating 16-row blocks; q0 is the item's first row within its
-// 128-row group (the group's rows are in that order, packed or not).
+// gate and up in alternating 16-row blocks; the item starts at row q0 of 128-row group
+// grp and may run on into the following groups (each group's rows are in that order,
+// packed or not, and consecutive groups hold consecutive activation columns).
 template <typename T, class Tile>
 __device__ __forceinline__ void gateup_item(const MoeArgs<T>& a, const int32_t* __restrict__ ids, char* smem, int e,
                                             int base, int rows, int grp, int q0) {
@@ -331,9 +332,10 @@ __device__ __forceinline__ void gateup_item(const MoeArgs<T>& a, const int32_t* 
   const int c0 = grp * (kPackRows / 2) + q0 / 2;  // activation columns [c0, c0 + kBN / 2)
   Tile t;
   const T* Wg = a.W_gu + (size_t)e * 2 * a.I * a.H;
-  if (a.packed) {  // the item's rows are rows q0 .. of packed group grp
-    const T* Wgrp = Wg + (size_t)grp * kPackRows * a.H;
-    t.set_b([&](int r) -> const T* { return Wgrp + (size_t)(q0 + r) * Tile::kBK; });
+  if (a.packed) {  // item row r is row (q0 + r) % 128 of packed group grp + (q0 + r) / 128
+    t.set_b([&](int r) -> const T* {
+      return Wg + (size_t)(grp + (q0 + r) / kPackRows) * kPackRows * a.H + (size_t)((q0 + r) % kPackRows) * Tile::kBK;
+    });
     t.bstride = (size_t)kPackRows * Tile::kRowBytes;
   } else {
     t.set_b([&](int r) -> const T* {
@@ -368,13 +370,13 @@ __device__ __forceinline__ void gateup_item(const MoeArgs<T>& a, const int32_t* 
   }
 }
 
-// BN = 128 weight rows per item (one 128-row group: 64 activation columns); with
-// SPLIT > 1 the tail items of moe_item run as SPLIT parts of BN / SPLIT rows (waves
+// BN weight rows per item (BN / 128 whole 128-row groups: BN / 2 activation columns);
+// with SPLIT > 1 the tail items of moe_item run as SPLIT parts of BN / SPLIT rows (waves
 // stacked along the rows when a part is too narrow to give every wave gate/up pairs).
 template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void moe_gateup_kernel(MoeArgs<T> a) {
-  static_assert(BN == kPackRows, "a gate/up item is one 128-row group");
+  static_assert(BN % kPackRows == 0, "a gate/up item is whole 128-row groups");
   using Tile = GemmTile<T, BM, BN, WM, WN, (BM <= 16 && kStreamFewRows)>;  // 16-row items: one item per weight tile
   constexpr bool kNarrow = BN / SPLIT < WN * 32;
   using Part = GemmTile<T, BM, BN / SPLIT, kNarrow ? WM * WN : WM, kNarrow ? 1 : WN, (BM <= 16 && kStreamFewRows)>;
@@ -387,14 +389,14 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
     off = sb.off;
     ids = sb.ids;
   }
-  int e, r0, n_e, j, part;  // j: the 128-row group (activation columns [64 j, 64 j + 64))
+  int e, r0, n_e, j, part;  // j: item along the rows (groups j * BN / 128 ..)
   if (!moe_item(off, a.E, BM, a.I / (BN / 2), SPLIT > 1 ? a.slots : 0, SPLIT, e, r0, n_e, j, part)) return;
   const int base = off[e] + r0;
   const int rows = min(BM, n_e - r0);
   if (SPLIT > 1 && part >= 0)
-    gateup_item<T, Part>(a, ids, smem, e, base, rows, j, part * (BN / SPLIT));
+    gateup_item<T, Part>(a, ids, smem, e, base, rows, j * (BN / kPackRows), part * (BN / SPLIT));
   else
-    gateup_item<T, Tile>(a, ids, smem, e, base, rows, j, 0);
+    gateup_item<T, Tile>(a, ids, smem, e, base, rows, j * (BN / kPackRows), 0);
 }
 
 // Down-projection epilogue: y = rnd(sum), routed = rnd(w * y), mlp = rnd(rnd(routed + hsb)
@@ -451,11 +453,10 @@ __device__ __forceinline__ void down_item(const MoeArgs<T>& a, char* smem, int e
   Tile t;
   t.set_a([&](int r) -> const T* { return a.neurons + (size_t)(base + min(r, rows - 1)) * a.I; });
   const T* Wd = a.W_dn + (size_t)e * a.H * a.I;
-  if (a.packed) {  // rows n0 .. n0 + kBN lie in packed group n0 / 128
-    static_assert(kPackRows % Tile::kBN == 0, "a down item lies in one packed row group");
-    const T* Wgrp = Wd + (size_t)(n0 / kPackRows) * kPackRows * a.I;
-    const int q0 = n0 % kPackRows;
-    t.set_b([&](int r) -> const T* { return Wgrp + (size_t)(q0 + r) * Tile::kBK; });
+  if (a.packed) {  // output row n is row n % 128 of packed group n / 128
+    t.set_b([&](int r) -> const T* {
+      return Wd + (size_t)((n0 + r) / kPackRows) * kPackRows * a.I + (size_t)((n0 + r) % kPackRows) * Tile::kBK;
+    });
     t.bstride = (size_t)kPackRows * Tile::kRowBytes;
   } else {
     t.set_b([&](int r) -> const T* { return Wd + (size_t)(n0 + r) * a.I; });
@@ -483,27 +484,28 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
     down_item<T, Tile>(a, smem, e, base, rows, c * BN);
 }
 
-// Workgroups of the 128 x 128 expert tiles resident on the current device at once (two
-// per CU), a multiple of 8; 0 if the device cannot be queried.
-static int moe_slots() {
+// Workgroups of the 128-row expert tiles resident on the current device at once (two
+// 4-wave or one 8-wave workgroup per CU), a multiple of 8; 0 if the device cannot be
+// queried.
+static int moe_slots(int waves) {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[kMaxDev];  // per device: 0 = not yet asked, else slots + 1
+  static std::atomic<int> cache[kMaxDev];  // per device: 0 = not yet asked, else CUs + 1
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < kMaxDev) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c - 1;
+  const int c = dev >= 0 && dev < kMaxDev ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (c > 0) {
+    cus = c - 1;
+  } else {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < kMaxDev) cache[dev].store(cus + 1, std::memory_order_relaxed);
   }
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const int slots = (2 * cus) / 8 * 8;
-  if (dev >= 0 && dev < kMaxDev) cache[dev].store(slots + 1, std::memory_order_relaxed);
-  return slots;
+  return (cus * (8 / waves)) / 8 * 8;  // eight waves of a CU are resident at once
 }
 
 template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
 static hipError_t launch_gateup_cfg(const MoeArgs<T>& a0, hipStream_t s) {
   MoeArgs<T> a = a0;
-  a.slots = SPLIT > 1 ? moe_slots() : 0;
+  a.slots = SPLIT > 1 ? moe_slots(WM * WN) : 0;
   hipLaunchKernelGGL((moe_gateup_kernel<T, BM, WM, WN, BN, SPLIT>), dim3(moe_grid(a.ntok, a.E, BM, a.I / (BN / 2), a.slots)),
                      dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
@@ -512,7 +514,7 @@ static hipError_t launch_gateup_cfg(const MoeArgs<T>& a0, hipStream_t s) {
 template <typename T, int BM, int WM, int WN, int BN = 128, int SPLIT = 1>
 static hipError_t launch_down_cfg(const MoeArgs<T>& a0, hipStream_t s) {
   MoeArgs<T> a = a0;
-  a.slots = SPLIT > 1 ? moe_slots() : 0;
+  a.slots = SPLIT > 1 ? moe_slots(WM * WN) : 0;
   hipLaunchKernelGGL((moe_down_kernel<T, BM, WM, WN, BN, SPLIT>), dim3(moe_grid(a.ntok, a.E, BM, a.H / BN, a.slots)),
                      dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
