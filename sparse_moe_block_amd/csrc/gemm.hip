@@ -146,15 +146,19 @@ struct EpiAt {
   }
 };
 
+// Tiles in raster order after the XCD remap: column tiles fastest (the A row band stays
+// in cache while B streams), or with m_fast row tiles fastest (B much larger than A:
+// each B column band is then read from memory once while the whole of A stays cached,
+// e.g. a tied vocabulary head).
 template <typename T, int BM, int BN, int WM, int WN, class Epi, int NST>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) void gemm_nt_kernel(const T* __restrict__ A, int lda, const T* __restrict__ B,
-                                                               int ldb, int M, int N, int K, Epi epi) {
+                                                               int ldb, int M, int N, int K, Epi epi, int m_fast) {
   using Tile = GemmTile<T, BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::kLdsBytes];
-  const int ntn = (N + BN - 1) / BN;
+  const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int m0 = (wg / ntn) * BM, n0 = (wg % ntn) * BN;
+  const int m0 = (m_fast ? wg % ntm : wg / ntn) * BM, n0 = (m_fast ? wg / ntm : wg % ntn) * BN;
   Tile t;
   t.set_a([&](int r) -> const T* { return A + (size_t)min(m0 + r, M - 1) * lda; });
   t.set_b([&](int r) -> const T* { return B + (size_t)min(n0 + r, N - 1) * ldb; });
@@ -165,8 +169,9 @@ __attribute__((amdgpu_waves_per_eu(GemmTile<T, BM, BN, WM, WN>::kWavesPerEU))) v
 template <typename T, int BM, int BN, int WM, int WN, class Epi, int NST = 3>
 static hipError_t launch_cfg(const T* A, int lda, const T* B, int ldb, int M, int N, int K, Epi epi, hipStream_t s) {
   const int g = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int m_fast = (long)N >= 8L * M;  // B at least 8x larger than A
   hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi, NST>), dim3(g), dim3(WM * WN * 64), 0, s, A, lda, B, ldb,
-                     M, N, K, epi);
+                     M, N, K, epi, m_fast);
   return hipGetLastError();
 }
 
