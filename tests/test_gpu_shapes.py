@@ -50,6 +50,13 @@ SHAPES = [
                            num_experts=4, moe_intermediate_size=128, seq=1600, batch=1)),
     ("d128_g1_split", dict(hidden_size=256, num_heads=2, num_kv_heads=2, head_dim=128, rope_dim=64,
                            num_experts=3, moe_intermediate_size=128, seq=1550, batch=1)),
+    # enough rows (2 x 1200, not a whole number of 128-row tiles) that q/k/v and o_proj
+    # take the 8-wave 128x192 tile, with widths that are not a whole number of it (q/k/v:
+    # 8 + 4 + 2 heads of 128 = 1792 columns; o_proj: 2048), so their last column tiles are
+    # ragged; o_proj keeps the model's reduction length (8 heads x 128). The grouped GEMMs'
+    # items (fewer than one round of resident workgroups) all run as half/quarter parts.
+    ("d128_g2_ragged_wide", dict(hidden_size=2048, num_heads=8, num_kv_heads=4, head_dim=128, rope_dim=64,
+                                 num_experts=4, moe_intermediate_size=512, seq=1200, batch=2)),
 ]
 
 
