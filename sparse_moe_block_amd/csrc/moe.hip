@@ -613,62 +613,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     else return *reinterpret_cast<const u32x4*>(p);
   };
   u32x4 q0[kF8Ahead], q1[kF8Ahead];
+  auto prefetch_w = [&]() {
 #pragma unroll
-  for (int p = 0; p < kF8Ahead; ++p) {
-    const int s = min(p, nds - 1);
-    q0[p] = wload(w0 + (size_t)s * wstep);
-    if (GATEUP) q1[p] = wload(w1 + (size_t)s * wstep);
-  }
+    for (int p = 0; p < kF8Ahead; ++p) {
+      const int s = min(p, nds - 1);
+      q0[p] = wload(w0 + (size_t)s * wstep);
+      if (GATEUP) q1[p] = wload(w1 + (size_t)s * wstep);
+    }
+  };
 
-  // stage the token rows (rows past the tile repeat its last row; never stored)
+  // stage the tile's token rows, eight 16-byte chunks per thread at a time; the weights'
+  // first loads go out right behind the first batch, so that batch waits for its own
+  // loads only. Only the tile's rows are loaded: the products of the rows past them read
+  // whatever LDS holds, and only those tokens' outputs (never stored) depend on them.
   {
     const int cpr = K / 8;  // 16-byte chunks per row
-    for (int c0 = threadIdx.x; c0 < kF8Tok * cpr; c0 += 256 * 8) {  // eight rows' loads in flight
+    const int nch = rows * cpr;
+    bool issued = false;
+    for (int c0 = threadIdx.x; c0 < nch; c0 += 256 * 8) {
       u32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int ch = c0 + u * 256;
-        if (ch < kF8Tok * cpr) {
-          const int r = ch / cpr, cc = ch % cpr;
-          const int rr = min(r, rows - 1);
-          const bf16_t* src = GATEUP ? a.hn + (size_t)ids[base + rr] * a.H : a.neurons + (size_t)(base + rr) * a.I;
-          v[u] = *reinterpret_cast<const u32x4*>(src + cc * 8);
-        }
+        const int ch = min(c0 + u * 256, nch - 1);
+        const int r = ch / cpr, cc = ch % cpr;
+        const bf16_t* src = GATEUP ? a.hn + (size_t)ids[base + r] * a.H : a.neurons + (size_t)(base + r) * a.I;
+        v[u] = *reinterpret_cast<const u32x4*>(src + cc * 8);
+      }
+      if (!issued) {
+        prefetch_w();
+        issued = true;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int ch = c0 + u * 256;
-        if (ch < kF8Tok * cpr) *reinterpret_cast<u32x4*>(xs + (ch / cpr) * pitch + (ch % cpr) * 16) = v[u];
+        if (ch < nch) *reinterpret_cast<u32x4*>(xs + (ch / cpr) * pitch + (ch % cpr) * 16) = v[u];
       }
     }
+    if (!issued) prefetch_w();  // threads with no chunk
   }
   __syncthreads();
 
   const char* xrow = xs + r16 * pitch + grp * 32;
   f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  for (int s0 = 0; s0 < nds; s0 += kF8Ahead) {
-#pragma unroll
-    for (int p = 0; p < kF8Ahead; ++p) {
-      const int s = s0 + p;
-      if (s < nds) {
-        const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(xrow + (size_t)s * 128));
-        const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(xrow + (size_t)s * 128 + 16));
-        bf16x8_t wa, wb;
-        f8x16_to_bf16(q0[p], wa, wb);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc0, 0, 0, 0);
-        if (GATEUP) {
-          f8x16_to_bf16(q1[p], wa, wb);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc1, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc1, 0, 0, 0);
-        }
-        // refill this slot kF8Ahead steps ahead (past the end: the last step again)
-        const int sn = min(s + kF8Ahead, nds - 1);
-        q0[p] = wload(w0 + (size_t)sn * wstep);
-        if (GATEUP) q1[p] = wload(w1 + (size_t)sn * wstep);
-      }
+  // step s with the codes in slot p, which is then refilled kF8Ahead steps ahead (past
+  // the end: the last step again)
+  auto kstep = [&](int s, int p) {
+    const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(xrow + (size_t)s * 128));
+    const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(xrow + (size_t)s * 128 + 16));
+    bf16x8_t wa, wb;
+    f8x16_to_bf16(q0[p], wa, wb);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc0, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc0, 0, 0, 0);
+    if (GATEUP) {
+      f8x16_to_bf16(q1[p], wa, wb);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc1, 0, 0, 0);
     }
+    const int sn = min(s + kF8Ahead, nds - 1);
+    q0[p] = wload(w0 + (size_t)sn * wstep);
+    if (GATEUP) q1[p] = wload(w1 + (size_t)sn * wstep);
+  };
+  // Whole rounds of kF8Ahead steps first, with no branch inside: the compiler's wait
+  // tracking then sees the same loads in flight on every path and waits for the oldest
+  // slot only (with a branch per step it waited for every load in flight, so nothing
+  // stayed ahead). Then the remaining steps.
+  int s0 = 0;
+  for (; s0 + kF8Ahead <= nds; s0 += kF8Ahead) {
+#pragma unroll
+    for (int p = 0; p < kF8Ahead; ++p) kstep(s0 + p, p);
   }
+#pragma unroll
+  for (int p = 0; p < kF8Ahead; ++p)
+    if (s0 + p < nds) kstep(s0 + p, p);
 
   // lane holds rows n = 16 wave + 4 grp + i of the item's 64, for token r16
   if (r16 >= rows) return;
