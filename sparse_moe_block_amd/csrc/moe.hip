@@ -622,34 +622,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     }
   };
 
-  // stage the tile's token rows, eight 16-byte chunks per thread at a time; the weights'
-  // first loads go out right behind the first batch, so that batch waits for its own
-  // loads only. Only the tile's rows are loaded: the products of the rows past them read
-  // whatever LDS holds, and only those tokens' outputs (never stored) depend on them.
+  // Stage the tile's token rows, 16 chunks of 16 bytes per thread a batch; the weights'
+  // first loads go out right behind the last batch's, so that batch waits for its own
+  // loads only and the weight loads are the only ones in flight when the products start.
+  // Only the tile's rows are loaded: the products of the rows past them read whatever LDS
+  // holds, and only those tokens' outputs (never stored) depend on them.
   {
+    constexpr int kSB = 16;
     const int cpr = K / 8;  // 16-byte chunks per row
     const int nch = rows * cpr;
-    bool issued = false;
-    for (int c0 = threadIdx.x; c0 < nch; c0 += 256 * 8) {
-      u32x4 v[8];
+    const int nb = (nch + kSB * 256 - 1) / (kSB * 256);  // batches, the same for every thread
+    u32x4 v[kSB];
+    auto load_batch = [&](int c0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kSB; ++u) {
         const int ch = min(c0 + u * 256, nch - 1);
         const int r = ch / cpr, cc = ch % cpr;
         const bf16_t* src = GATEUP ? a.hn + (size_t)ids[base + r] * a.H : a.neurons + (size_t)(base + r) * a.I;
         v[u] = *reinterpret_cast<const u32x4*>(src + cc * 8);
       }
-      if (!issued) {
-        prefetch_w();
-        issued = true;
-      }
+    };
+    auto store_batch = [&](int c0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kSB; ++u) {
         const int ch = c0 + u * 256;
         if (ch < nch) *reinterpret_cast<u32x4*>(xs + (ch / cpr) * pitch + (ch % cpr) * 16) = v[u];
       }
+    };
+    for (int bi = 0; bi + 1 < nb; ++bi) {
+      load_batch((int)threadIdx.x + bi * kSB * 256);
+      store_batch((int)threadIdx.x + bi * kSB * 256);
     }
-    if (!issued) prefetch_w();  // threads with no chunk
+    load_batch((int)threadIdx.x + (nb - 1) * kSB * 256);
+    prefetch_w();
+    store_batch((int)threadIdx.x + (nb - 1) * kSB * 256);
   }
   __syncthreads();
 
@@ -672,6 +678,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int sn = min(s + kF8Ahead, nds - 1);
     q0[p] = wload(w0 + (size_t)sn * wstep);
     if (GATEUP) q1[p] = wload(w1 + (size_t)sn * wstep);
+    // steps stay in order: the scheduler would otherwise convert later slots' codes
+    // first, and wait for every load in flight to do so
+    __builtin_amdgcn_sched_barrier(0);
   };
   // Whole rounds of kF8Ahead steps first, with no branch inside: the compiler's wait
   // tracking then sees the same loads in flight on every path and waits for the oldest
