@@ -299,7 +299,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int kp = k0 + kb * 16 + 4 * grp + i;
-            if (kp > qp || (W >= 0 && qp - kp > W)) s[qb][kb][i] = -INFINITY;
+            // bitwise, not short-circuit: a select per score instead of a branch
+            const bool cut = (kp > qp) | ((W >= 0) & (qp - kp > W));
+            s[qb][kb][i] = cut ? -INFINITY : s[qb][kb][i];
             mx = fmaxf(mx, s[qb][kb][i]);
           }
       }
@@ -630,7 +632,9 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kp = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (kp > qp || (W >= 0 && qp - kp > W)) s[kb][r] = -INFINITY;
+          // bitwise, not short-circuit: a select per score instead of a branch
+          const bool cut = (kp > qp) | ((W >= 0) & (qp - kp > W));
+          s[kb][r] = cut ? -INFINITY : s[kb][r];
         }
     }
     float mx = -INFINITY;
