@@ -261,6 +261,14 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
   const float sqrt_d = sqrtf((float)d);
   const float temp = Act<T>::tof(a.temp[g]);
   const double inv_freq = p < r / 2 ? pow((double)a.theta, -2.0 * (double)p / (double)r) : 0.0;
+  // rotary angle of this lane's token, (L0 + t) inv_freq, as (cos, sin) in fp64: one
+  // sincos for the wave's first token, then a rotation by the angle of the 4 tpw tokens
+  // between the wave's steps (angle addition; fp64 keeps the drift far below fp32)
+  double cd = 1.0, sd = 0.0, cstep = 1.0, sstep = 0.0;
+  if (p < r / 2) {
+    sincos((double)(L0 + t0 + wave * tpw + sub) * inv_freq, &sd, &cd);
+    sincos((double)(4 * tpw) * inv_freq, &sstep, &cstep);
+  }
   for (int base = t0 + wave * tpw; base < t_end; base += 4 * tpw) {
     const int t = base + sub;
     const bool active = t < t_end;
@@ -289,12 +297,11 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
     }
     const float ka = conv(kca) + rka / (float)G;
     const float kb = conv(kcb) + rkb / (float)G;
-    float cs = 1.f, sn = 0.f;
-    if (p < r / 2) {
-      double sd, cd;
-      sincos((double)(L0 + tt) * inv_freq, &sd, &cd);
-      cs = (float)cd;
-      sn = (float)sd;
+    const float cs = (float)cd, sn = (float)sd;  // (1, 0) past the rotary dims
+    {
+      const double c2 = cd * cstep - sd * sstep;
+      sd = sd * cstep + cd * sstep;
+      cd = c2;
     }
     T* ob = outs + (wave * tpw + sub) * (G + 2) * d;
     // squared lengths of the G query heads and the key head, reduced together
