@@ -961,9 +961,7 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnArgs<T> a, 
   for (int c = 0; c < kBatch; ++c)
 #pragma unroll
     for (int j = 0; j < DPL; ++j) ov[c][j] = c < nchunk ? pl[c * stride + j] : 0.f;
-  float M = fmaxf(m2[0], m2[1]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float M = wave_max(fmaxf(m2[0], m2[1]));
   float lpart = 0.f;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {

@@ -310,9 +310,7 @@ __global__ __launch_bounds__(256) void cca_kernel(CcaArgs<T> a) {
     for (int hh = 0; hh < G; ++hh) ss[hh] = qa[hh] * qa[hh] + qb[hh] * qb[hh];
     ss[G] = ka * ka + kb * kb;
 #pragma unroll
-    for (int o = spt / 2; o > 0; o >>= 1)
-#pragma unroll
-      for (int i = 0; i <= G; ++i) ss[i] += __shfl_xor(ss[i], o, 64);
+    for (int i = 0; i <= G; ++i) ss[i] = lane_group_sum<spt>(ss[i]);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float sc = sqrt_d / fmaxf(sqrtf(ss[hh]), 1e-12f);

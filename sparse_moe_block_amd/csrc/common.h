@@ -128,22 +128,36 @@ template <> struct Mfma<float> {
   }
 };
 
-// Wave-wide reductions (wave64).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Reductions over aligned groups of N lanes (N a power of two, 2 .. 64); every lane of a
+// group ends with the same result. Inside a 16-lane row the partners come from DPP moves
+// (lane ^ 1 and ^ 2 by quad permutes, then the mirror of each 8-lane half and of the
+// row, each pairing one half's lanes with the other's), which stay in the vector ALU;
+// the steps across rows are cross-lane reads.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int N, class Op>
+__device__ __forceinline__ float lane_group_reduce(float v, Op op) {
+  static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "group of 2 .. 64 lanes");
+  v = op(v, dpp_mov<0xB1>(v));                          // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) v = op(v, dpp_mov<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v = op(v, dpp_mov<0x141>(v));   // row_half_mirror
+  if constexpr (N >= 16) v = op(v, dpp_mov<0x140>(v));  // row_mirror
+  if constexpr (N >= 32) v = op(v, __shfl_xor(v, 16, 64));
+  if constexpr (N >= 64) v = op(v, __shfl_xor(v, 32, 64));
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) { return lane_group_reduce<N>(v, OpAdd{}); }
+__device__ __forceinline__ float wave_sum(float v) { return lane_group_reduce<64>(v, OpAdd{}); }
+__device__ __forceinline__ float wave_max(float v) { return lane_group_reduce<64>(v, OpMax{}); }
 
 // Non-contracted fp32 ops: the residual stream is float32 op by op.
 __device__ __forceinline__ float fadd(float a, float b) { return __fadd_rn(a, b); }
