@@ -872,7 +872,7 @@ __global__ __launch_bounds__(64 * G) void attn_decode_kernel(AttnArgs<T> a, floa
     m_run = m_new;
     if constexpr (kDot2) {
       // key pairs (2m, 2m+1): the lane of key 2m packs both probabilities
-      const float pnext = __shfl_down(pv, 1, 64);
+      const float pnext = dpp_mov<0xF5>(pv);  // quad_perm [1, 1, 3, 3]: lane 2m reads lane 2m + 1
       if (!(lane & 1)) p2_s[wave][lane >> 1] = pack_bf16x2(pv, pnext);
     } else {
       p_s[wave][lane] = pv;

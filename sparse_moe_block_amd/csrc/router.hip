@@ -19,6 +19,8 @@
 // makes (router state first, then biases, then weights) is issued at its start, so
 // the whole kernel waits for memory about once; the selection runs in registers, 16
 // lanes per token.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -119,18 +121,36 @@ __device__ __forceinline__ void router_fc(const RouterFcFrags<T>& W, const T* in
   }
 }
 
-// Selection for one token: lanes 16 g .. 16 g + 15 of a wave hold the token's classes
-// c = lane % 16 and 16 + lane % 16. Softmax in fp64 over the fp32 logits (max and sum by
-// shuffles inside the 16-lane group), probabilities rounded to fp32, plus the balancing
-// biases in fp32; the first (lowest-index) maximum wins.
+// Selection for one token: lanes 16 g .. 16 g + 15 of a wave (one DPP row) hold the
+// token's classes c = lane % 16 and 16 + lane % 16. Softmax in fp64 over the fp32 logits,
+// probabilities rounded to fp32, plus the balancing biases in fp32; the first
+// (lowest-index) maximum wins. The row's max, sum and arg-max pair lanes by DPP moves
+// (lane ^ 1, ^ 2, then the mirrors of the 8-lane halves and of the row), so every lane of
+// the row ends with the same result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)dpp_mov_i<CTRL>((int)(unsigned)u);
+  const unsigned hi = (unsigned)dpp_mov_i<CTRL>((int)(unsigned)(u >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+template <class F>
+__device__ __forceinline__ void row16_steps(F step) {
+  step(std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  step(std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{});  // row_mirror
+}
 __device__ __forceinline__ double group16_max(double v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 16));
+  row16_steps([&](auto c) { v = fmax(v, dpp_mov_f64<decltype(c)::value>(v)); });
   return v;
 }
 __device__ __forceinline__ double group16_sum(double v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+  row16_steps([&](auto c) { v += dpp_mov_f64<decltype(c)::value>(v); });
   return v;
 }
 
@@ -294,12 +314,13 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(RouterArgs<T>
     float bs = s1, bp = p1;
     int bc = c1;
     if (s2 > s1) { bs = s2; bp = p2; bc = c2; }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      const float os = __shfl_xor(bs, o, 16), op = __shfl_xor(bp, o, 16);
-      const int oc = __shfl_xor(bc, o, 16);
+    row16_steps([&](auto c) {
+      constexpr int kc = decltype(c)::value;
+      const float os = __int_as_float(dpp_mov_i<kc>(__float_as_int(bs)));
+      const float op = __int_as_float(dpp_mov_i<kc>(__float_as_int(bp)));
+      const int oc = dpp_mov_i<kc>(bc);
       if (os > bs || (os == bs && oc < bc)) { bs = os; bp = op; bc = oc; }
-    }
+    });
     if (r16 == 0) {
       cls_s[t] = bc;
       if (tok < a.ntok) {
