@@ -450,9 +450,14 @@ __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a
 
 // ----------------------------------------------------------------------------- prefill, bf16, d = 128
 //
-// A second prefill kernel for bf16 with head_dim 128: one workgroup per CU of 2 G waves,
-// two per query head of the KV group, each wave 32 of the workgroup's 64 queries (two
-// waves per SIMD). Both products use the 32x32x16 MFMA:
+// A second prefill kernel for bf16 with head_dim 128. A unit is (64-query tile, chunk of
+// its key tiles, KV group, sequence); each wave takes 32 of those queries for one query
+// head of the group. QH query halves per workgroup: with 4 heads a group (the ZAYA1
+// shape) a workgroup takes one half (4 waves) and two workgroups share a CU, so each
+// SIMD runs two waves of different workgroups whose steps drift apart and one's softmax
+// overlaps the other's products (measured 71.1 -> 68 us at 4096 tokens against one
+// 8-wave workgroup per CU with both halves, whose waves met at every step's barrier);
+// with 1 or 2 heads both halves share a workgroup. Both products use the 32x32x16 MFMA:
 //   S^T = K Q^T  in 32-key x 32-query blocks: lane l holds query l % 32 and the keys
 //                8 (r / 4) + 4 (l / 32) + r % 4, r < 16, of the block;
 //   O^T = V^T P^T in 32-dim x 32-query blocks over 16-key steps: the B operand of step
@@ -463,9 +468,9 @@ __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a
 // K and V tiles go from global memory straight into LDS (global_load_lds, row-major
 // [key][dim], a 16-byte-chunk swizzle applied on the global side) through a ring of LDS
 // slots declared as separate arrays (so the compiler's wait tracking sees that the loads
-// into one slot cannot alias reads of another): three slots, two tiles ahead of the
-// products, with 4 heads a group (one workgroup per CU); two slots, one tile ahead,
-// otherwise (two workgroups per CU fit only then). The V^T operands come from the row-major V tile through the LDS transpose
+// into one slot cannot alias reads of another): two slots, one tile ahead of the
+// products, so two workgroups fit a CU (three slots, two tiles ahead, serve an 8-wave
+// workgroup alone on its CU). The V^T operands come from the row-major V tile through the LDS transpose
 // read (ds_read_b64_tr_b16): within each 16-lane group, lane a + 4 k addresses 4 dims
 // of key row k and lane 4 a + c receives dim c of that chunk for the 4 keys. Each wave
 // waits only for the tile the next step reads (the newest tile's loads stay in flight)
@@ -503,13 +508,13 @@ __device__ __forceinline__ uint2 read_tr(const char* p) {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 }  // namespace pf64
 
-template <int G>
-__global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill64_kernel(
+template <int G, int QH>
+__global__ __launch_bounds__(64 * QH * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill64_kernel(
     AttnArgs<bf16_t> a, float* __restrict__ part, int NC) {
   using namespace pf64;
-  constexpr int NW = 2 * G;                // waves
-  constexpr int NSLOT = G == 4 ? 3 : 2;    // ring slots; tiles in flight ahead: NSLOT - 1
-  constexpr int kLoads = 8 / G;            // 16-byte load instructions per thread per K (or V) tile
+  constexpr int NW = QH * G;                          // waves
+  constexpr int NSLOT = (G == 4 && QH == 2) ? 3 : 2;  // ring slots; tiles in flight ahead: NSLOT - 1
+  constexpr int kLoads = 16 / NW;  // 16-byte load instructions per thread per K (or V) tile
   constexpr int kTileLoads = 2 * kLoads;   // per thread per tile (K and V)
   constexpr int kPendOk = (NSLOT - 2) * kTileLoads;  // loads that may stay in flight at a step's end
   static_assert(NW * kLoads * 4 == 64, "one tile: 64 rows of 4 per instruction");
@@ -517,12 +522,14 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(1024))) char lds1[kBuf];
   __shared__ __attribute__((aligned(1024))) char lds2[NSLOT == 3 ? kBuf : 16];
 
-  // units heaviest first over the whole grid: (query tile from the last, chunk), then
-  // KV group and sequence fastest, so the longest units of every group and sequence
-  // start in the first round
+  // units heaviest first over the whole grid: (query tile from the last, chunk, query
+  // half when a workgroup takes one), then KV group and sequence fastest, so the longest
+  // units of every group and sequence start in the first round
   const int nqb = (a.S + kQW - 1) / kQW;
   const int ngb = a.nkv * a.B;
-  const int gb = (int)blockIdx.x % ngb, r = (int)blockIdx.x / ngb;
+  const int gb = (int)blockIdx.x % ngb;
+  const int r = QH == 2 ? (int)blockIdx.x / ngb : (int)blockIdx.x / ngb / 2;
+  const int half = QH == 2 ? 0 : ((int)blockIdx.x / ngb) % 2;
   const int c = r % NC;
   const int qblk = nqb - 1 - r / NC;
   const int g = gb % a.nkv, b = gb / a.nkv;
@@ -534,7 +541,7 @@ __global__ __launch_bounds__(128 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int hg = wave % G, qh = wave / G;  // head within the group, query half
+  const int hg = wave % G, qh = QH == 2 ? wave / G : half;  // head within the group, query half
   const int h = g * G + hg;
   const int row = qh * 32 + l32;           // this lane's query within the tile
   const int q0 = qt.q0, qp_min = qt.qp_min, qp_max = qt.qp_max;
@@ -1003,7 +1010,9 @@ template <typename T, int D, int G>
 static hipError_t launch_prefill_dg(const AttnArgs<T>& a, float* part, int NC, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && D == 128 && G <= 4) {
     const int nqb = (a.S + pf64::kQW - 1) / pf64::kQW;
-    hipLaunchKernelGGL((attn_prefill64_kernel<G>), dim3(nqb * NC * a.nkv * a.B), dim3(128 * G), 0, s, a, part, NC);
+    constexpr int QH = G == 4 ? 1 : 2;  // query halves per workgroup
+    hipLaunchKernelGGL((attn_prefill64_kernel<G, QH>), dim3(nqb * NC * a.nkv * a.B * (2 / QH)), dim3(64 * QH * G), 0,
+                       s, a, part, NC);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || NC == 1) return e;
     using CS = CombineShape<D, G>;
