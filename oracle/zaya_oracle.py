@@ -30,7 +30,11 @@ design notes; each is flagged at the line that takes it ("reading: ...").
 Parity vs the trained ZAYA1 model is unpinned (no weights or reference
 activations exist here); every function is pinned by the tests under
 ``tests/test_oracle_*.py`` against closed forms, invariants, brute force and the
-pages' own identities.
+pages' own identities, except two orderings that rest on the pages' wording alone
+(parity unpinned: no check can tell them from the alternatives without the trained
+model): ``embed`` adds the shift before it multiplies by the scale ("after its shift
+and scale"), and ``stream_norm`` rounds the float32 stream to the act dtype before
+it norms it ("cast the stream to their weight's dtype before they norm it").
 """
 from __future__ import annotations
 
