@@ -415,16 +415,12 @@ __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a
   const size_t unit0 = (((size_t)b * a.nkv + g) * nqb + qblk) * NC;
   const size_t ustride = (size_t)G * QW * (D + 2);
   const float* base = part + (unit0 * G + wave) * QW * (D + 2) + (size_t)row * (D + 2);
-  // chunks in groups of four, loads issued together (past the last chunk they re-read it)
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < qt.nc; c0 += 4) {
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) M = fmaxf(M, base[min(c0 + cc, qt.nc - 1) * ustride + D]);
-  }
-  float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < qt.nc; c0 += 4) {
-    float mc[4], lc[4];
-    float4 v[4];
+  // chunks in groups of four, loads issued together (past the last chunk they re-read it).
+  // The first group's maxima, sums and outputs are all requested at once, so with at most
+  // four chunks the pass waits for memory once; later groups' maxima follow.
+  float mc[4], lc[4];
+  float4 v[4];
+  auto load_group = [&](int c0) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const int ci = min(c0 + cc, qt.nc - 1);
@@ -432,6 +428,16 @@ __global__ __launch_bounds__(256) void attn_prefill_combine_kernel(AttnArgs<T> a
       lc[cc] = base[ci * ustride + D + 1];
       v[cc] = *reinterpret_cast<const float4*>(base + ci * ustride + 4 * j);
     }
+  };
+  load_group(0);
+  float M = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+  for (int c0 = 4; c0 < qt.nc; c0 += 4) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) M = fmaxf(M, base[min(c0 + cc, qt.nc - 1) * ustride + D]);
+  }
+  float lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < qt.nc; c0 += 4) {
+    if (c0 > 0) load_group(c0);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const float sc = (c0 + cc >= qt.nc || mc[cc] == -INFINITY) ? 0.f : exp2f(mc[cc] - M);
